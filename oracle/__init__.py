@@ -1,0 +1,27 @@
+"""CPU oracle for causal block-sparse attention forward — TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, obviously-correct definition of what the GPU
+path computes, written in numpy float64 from the source pages:
+
+* ``routes``  — the per-query-block key-block sets (BF1 causal dyadic route,
+  the BSBR within-chunk block-diagonal route, the dense causal route and a
+  seeded static-random nonlocal graph), their CSR encoding, and graph
+  properties (selected token pairs, shortest-path depth).
+* ``attn``    — block-sparse attention as masked dense softmax attention:
+  the route is expanded to an explicit token mask which is applied before the
+  softmax, so excluded pairs get weight exactly zero.
+
+Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``.  The product path (the C-ABI library and
+its Python binding in ``long_context_block_amd``) never imports, calls or
+links anything here, and nothing here imports the product path.  The two
+share only the seeded input generators in ``synth.py`` (which hold none of the
+method's arithmetic).
+
+Pins (what ties this oracle to something other than itself) live in
+``tests/test_oracle_routes.py`` and ``tests/test_oracle_attn.py``; each function
+below names the passage it follows.  Functions with no pin say "parity
+unpinned" in their docstring.
+"""
+
+from . import routes, attn  # noqa: F401

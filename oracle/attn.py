@@ -1,0 +1,111 @@
+"""Block-sparse attention as masked dense softmax attention — oracle, fp64, CPU.
+
+Definition followed ("Block-Sparse Attention", "Math Or Compute Schema": the
+block mask is applied before the softmax so that only selected query-block ×
+key-block regions carry weight; "How It Works": skipped blocks are never
+scored; the per-head formula softmax(Q_i K_i^T / sqrt(d_k)) V_i):
+
+    M[t, s] = (block(s) in R(block(t))) and (s <= t) and (s < n) and (t < n)
+    S       = Q K^T * scale                      (scale = 1/sqrt(d) by default)
+    S[~M]   = -inf
+    P       = exp(S - rowmax S) / rowsum         (excluded pairs get exactly 0)
+    O       = P V
+
+Readings of the pages used here:
+
+* the mask is additive -inf (weight exactly zero), not a 0/1 product with the
+  scores — the product form printed in the formula would leave weight e^0 on
+  excluded pairs, which contradicts "skipped blocks are never scored";
+* causality inside a block: a query block reads itself causally ("BF1 ...",
+  Method; "bsbr", Solution, the within-chunk causal mask M_in), i.e. s <= t;
+* grouped-query attention (not on the pages): query head h reads key/value
+  head floor(h / G), G = heads_q / heads_kv;
+* inputs of any float dtype are converted exactly to float64 first, so the
+  oracle sees the same rounded values the GPU path reads.
+
+Rows are processed one query row-panel at a time (softmax is row-wise, so
+this is the definition, not a reformulation) to bound memory.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def _to_f64(x) -> np.ndarray:
+    """Exact conversion of a torch tensor (any float dtype) or array to float64."""
+    if hasattr(x, "detach"):
+        return x.detach().to("cpu").double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def token_mask(n: int, B: int, row_ptr, col_idx, rows) -> np.ndarray:
+    """Boolean mask M[len(rows), n] for the given query token indices."""
+    rows = np.asarray(rows, dtype=np.int64)
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    nqb = len(rp) - 1
+    blk_allowed = np.zeros((nqb, nqb), dtype=bool)
+    for i in range(nqb):
+        blk_allowed[i, ci[rp[i]:rp[i + 1]]] = True
+    s = np.arange(n, dtype=np.int64)
+    m = blk_allowed[(rows // B)[:, None], (s // B)[None, :]]
+    m &= s[None, :] <= rows[:, None]
+    return m
+
+
+def attention(q, k, v, B: int, row_ptr, col_idx, scale: float | None = None,
+              rows=None, return_lse: bool = False):
+    """Masked-dense fp64 attention.
+
+    q: [batch, Hq, n, d]; k, v: [batch, Hkv, n, d] (torch tensors or arrays).
+    rows: optional 1-D array of query token indices to evaluate (default all).
+    Returns O [batch, Hq, len(rows), d] in float64 (and LSE [batch, Hq, len(rows)]
+    = scale*max + log(sum) in natural log when ``return_lse``).
+    """
+    Q, K, V = _to_f64(q), _to_f64(k), _to_f64(v)
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if hq % hkv:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    G = hq // hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((b, hq, len(rows), d), dtype=np.float64)
+    lse = np.empty((b, hq, len(rows)), dtype=np.float64)
+    # one panel per query block touched by `rows`
+    blocks = rows // B
+    for blk in np.unique(blocks):
+        sel = np.nonzero(blocks == blk)[0]
+        r = rows[sel]
+        M = token_mask(n, B, row_ptr, col_idx, r)
+        for bi in range(b):
+            for h in range(hq):
+                kv = h // G
+                S = (Q[bi, h, r, :] @ K[bi, kv].T) * scale
+                S = np.where(M, S, -np.inf)
+                mx = S.max(axis=1, keepdims=True)
+                E = np.exp(S - mx)
+                den = E.sum(axis=1, keepdims=True)
+                P = E / den
+                out[bi, h, sel, :] = P @ V[bi, kv]
+                lse[bi, h, sel] = mx[:, 0] + np.log(den[:, 0])
+    return (out, lse) if return_lse else out
+
+
+def attention_probs(q, k, B: int, row_ptr, col_idx, scale: float | None = None):
+    """The attention weights P [batch, Hq, n, n] (small n only; used by the pins)."""
+    Q, K = _to_f64(q), _to_f64(k)
+    b, hq, n, d = Q.shape
+    G = hq // K.shape[1]
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    M = token_mask(n, B, row_ptr, col_idx, np.arange(n))
+    P = np.empty((b, hq, n, n))
+    for bi in range(b):
+        for h in range(hq):
+            S = np.where(M, (Q[bi, h] @ K[bi, h // G].T) * scale, -np.inf)
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            P[bi, h] = E / E.sum(axis=1, keepdims=True)
+    return P

@@ -1,0 +1,175 @@
+"""Pins for the oracle's masked-dense attention (CPU only).
+
+Ties oracle/attn.py to a library routine (torch's scaled_dot_product_attention
+in float64 for the dense-causal and per-chunk reductions), to invariants of the
+softmax (rows sum to one, exact zeros outside the route), to closed forms
+(uniform weights when K = 0, single-key rows) and to a pure-Python scalar
+brute force on tiny inputs whose route membership is restated independently.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import attn as A
+from oracle import routes as R
+
+KINDS = [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM]
+
+
+def _qkv(b, hq, hkv, n, d, seed=0, dtype=torch.float64):
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(b, hq, n, d, generator=g, dtype=torch.float64).to(dtype)
+    k = torch.randn(b, hkv, n, d, generator=g, dtype=torch.float64).to(dtype)
+    v = torch.randn(b, hkv, n, d, generator=g, dtype=torch.float64).to(dtype)
+    return q, k, v
+
+
+def _pow2(x):
+    return x > 0 and (x & (x - 1)) == 0
+
+
+def _member(kind, i, j, nl=2):
+    """Block membership restated without oracle.routes (static-random excepted)."""
+    if kind == R.BF1:
+        off = i - j
+        return 0 <= j <= i and (off <= nl or _pow2(off) or j == 0)
+    if kind == R.BLOCK_DIAGONAL:
+        return i == j
+    if kind == R.DENSE_CAUSAL:
+        return 0 <= j <= i
+    return j in R.static_random_set(i, 14, 17, True)
+
+
+@pytest.mark.parametrize("n,B", [(256, 32), (100, 16)])
+def test_dense_route_is_causal_sdpa(n, B):
+    q, k, v = _qkv(2, 3, 3, n, 16, seed=1)
+    rp, ci = R.route_csr(R.DENSE_CAUSAL, n, B)
+    got = A.attention(q, k, v, B, rp, ci)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True).numpy()
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_explicit_scale_matches_sdpa():
+    q, k, v = _qkv(1, 2, 2, 64, 8, seed=2)
+    rp, ci = R.route_csr(R.DENSE_CAUSAL, 64, 16)
+    got = A.attention(q, k, v, 16, rp, ci, scale=0.3)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=0.3).numpy()
+    assert np.abs(got - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("n,B", [(256, 32), (96, 16)])
+def test_block_diagonal_is_per_chunk_attention(n, B):
+    q, k, v = _qkv(2, 2, 2, n, 16, seed=3)
+    rp, ci = R.route_csr(R.BLOCK_DIAGONAL, n, B)
+    got = A.attention(q, k, v, B, rp, ci)
+    for c in range(n // B):
+        sl = slice(c * B, (c + 1) * B)
+        ref = F.scaled_dot_product_attention(q[:, :, sl], k[:, :, sl], v[:, :, sl], is_causal=True).numpy()
+        assert np.abs(got[:, :, sl] - ref).max() < 1e-12
+    # permuting chunks permutes the outputs identically
+    perm = np.random.default_rng(0).permutation(n // B)
+    idx = np.concatenate([np.arange(p * B, (p + 1) * B) for p in perm])
+    got_p = A.attention(q[:, :, idx], k[:, :, idx], v[:, :, idx], B, rp, ci)
+    assert np.abs(got_p - got[:, :, idx]).max() < 1e-12
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_probs_rows_sum_to_one_and_exact_zeros(kind):
+    n, B = 72, 8
+    q, k, v = _qkv(1, 2, 1, n, 8, seed=4)
+    rp, ci = R.route_csr(kind, n, B)
+    P = A.attention_probs(q, k, B, rp, ci)
+    assert np.abs(P.sum(-1) - 1).max() < 1e-12
+    for t in range(n):
+        for s in range(n):
+            inside = s <= t and _member(kind, t // B, s // B)
+            if inside:
+                assert (P[:, :, t, s] > 0).all()
+            else:
+                assert (P[:, :, t, s] == 0.0).all()
+
+
+def _brute(q, k, v, B, kind, scale, G):
+    """Pure-Python scalar triple loop with math.exp."""
+    b, hq, n, d = q.shape
+    out = np.zeros((b, hq, n, d))
+    for bi in range(b):
+        for h in range(hq):
+            kv = h // G
+            for t in range(n):
+                sel = [s for s in range(t + 1) if _member(kind, t // B, s // B)]
+                sc = [scale * sum(float(q[bi, h, t, e]) * float(k[bi, kv, s, e]) for e in range(d)) for s in sel]
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                den = sum(w)
+                for e in range(d):
+                    out[bi, h, t, e] = sum(w[a] * float(v[bi, kv, s, e]) for a, s in enumerate(sel)) / den
+    return out
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n,B", [(64, 8), (37, 4), (37, 8)])
+def test_brute_force_tiny(kind, n, B):
+    q, k, v = _qkv(1, 2, 1, n, 5, seed=5)
+    rp, ci = R.route_csr(kind, n, B)
+    got = A.attention(q, k, v, B, rp, ci)
+    ref = _brute(q, k, v, B, kind, 1 / math.sqrt(5), 2)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_uniform_weights_when_k_is_zero(kind):
+    # K = 0 makes every selected score 0, so O[t] is the plain mean of V over the selected keys.
+    n, B = 300, 16
+    q, _, _ = _qkv(1, 1, 1, n, 4, seed=6)
+    k = torch.zeros(1, 1, n, 4, dtype=torch.float64)
+    s = torch.arange(n, dtype=torch.float64)
+    v = torch.stack([torch.ones(n), s, s * s, torch.zeros(n)], -1)[None, None]
+    rp, ci = R.route_csr(kind, n, B)
+    got, lse = A.attention(q, k, v, B, rp, ci, return_lse=True)
+    for t in range(n):
+        sel = [x for x in range(t + 1) if _member(kind, t // B, x // B)]
+        assert abs(got[0, 0, t, 0] - 1.0) < 1e-12
+        assert abs(got[0, 0, t, 1] - np.mean(sel)) < 1e-9
+        assert abs(got[0, 0, t, 2] - np.mean(np.square(sel))) < 1e-6 * max(1.0, np.mean(np.square(sel)))
+        assert abs(lse[0, 0, t] - math.log(len(sel))) < 1e-12
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_first_row_reads_only_itself(kind):
+    q, k, v = _qkv(2, 2, 2, 40, 8, seed=7)
+    rp, ci = R.route_csr(kind, 40, 8)
+    got = A.attention(q, k, v, 8, rp, ci)
+    assert np.array_equal(got[:, :, 0], v[:, :, 0].numpy())
+
+
+def test_gqa_equals_repeated_kv():
+    q, k, v = _qkv(1, 6, 2, 48, 8, seed=8)
+    rp, ci = R.route_csr(R.BF1, 48, 8)
+    got = A.attention(q, k, v, 8, rp, ci)
+    ref = A.attention(q, k.repeat_interleave(3, dim=1), v.repeat_interleave(3, dim=1), 8, rp, ci)
+    assert np.array_equal(got, ref)
+    # and not the tiled (h % Hkv) mapping
+    alt = A.attention(q, k.repeat(1, 3, 1, 1), v.repeat(1, 3, 1, 1), 8, rp, ci)
+    assert np.abs(alt - got).max() > 1e-3
+
+
+def test_rows_subset_matches_full():
+    q, k, v = _qkv(1, 2, 2, 130, 8, seed=9)
+    rp, ci = R.route_csr(R.STATIC_RANDOM, 130, 16)
+    full = A.attention(q, k, v, 16, rp, ci)
+    rows = np.array([0, 5, 17, 64, 129])
+    part = A.attention(q, k, v, 16, rp, ci, rows=rows)
+    assert np.abs(part - full[:, :, rows]).max() < 1e-13  # same rows, different BLAS blocking
+
+
+def test_bf16_inputs_are_read_exactly():
+    q, k, v = _qkv(1, 1, 1, 32, 8, seed=10, dtype=torch.bfloat16)
+    rp, ci = R.route_csr(R.BF1, 32, 8)
+    a = A.attention(q, k, v, 8, rp, ci)
+    b = A.attention(q.double(), k.double(), v.double(), 8, rp, ci)
+    assert np.array_equal(a, b)
