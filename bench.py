@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark: causal block-sparse attention forward (prefill) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_32k] [--no-cpu-baseline]
+
+Workload (default): the Qwen3-0.6B-shaped layer at 32K tokens — batch 1, 16 query / 8 key-value
+heads, d = 128, block 128, bf16, BF1 route — the geometry the BF1 summary quotes its 32K
+per-layer prefill speedup on.  Inputs are seeded N(0, 1) synthetic tensors already resident in
+HBM when timing starts.
+
+One step = one pass of the hot path: build the BF1 route (integer kernels) and run the
+block-sparse forward over it.  W untimed warmup steps, then exactly K steps between HIP events
+on the launch stream, bracketed by torch.cuda.synchronize().  Separately timed on the same
+inputs: the forward alone (the dominant kernel, for the roofline), and the same kernel over the
+dense causal route (the speedup denominator), in both orders sparse->dense and dense->sparse.
+
+Prints ONE JSON line.  value = selected-interaction TFLOP/s of the step, where selected FLOPs =
+4 * d * batch * heads_q * S and S counts the causal token pairs the route selects (QK^T and PV
+only, the diagonal included).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak (published)
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (published)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def selected_pairs(row_ptr: np.ndarray, col_idx: np.ndarray, n: int, B: int) -> int:
+    """Causal token pairs selected by a CSR route (closed form per block pair)."""
+    total = 0
+    nqb = len(row_ptr) - 1
+    for i in range(nqb):
+        ti = min(B, n - i * B)
+        for j in col_idx[row_ptr[i]:row_ptr[i + 1]]:
+            j = int(j)
+            if j < i:
+                total += ti * min(B, n - j * B)
+            elif j == i:
+                total += ti * (ti + 1) // 2
+    return total
+
+
+def time_loop(fn, steps: int, warmup: int):
+    """Average ms per call over `steps` calls, timed with events on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def per_call_samples(fn, reps: int):
+    """Per-call durations (ms) from event pairs around each call: median/p10/p90 reporting."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
+    """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload."""
+    from oracle import attn as A
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    nqb = w.nqb
+    order = np.linspace(0, nqb - 1, num=min(nqb, 64)).round().astype(int)
+    done_rows, sel_pairs, t_used, blocks = 0, 0, 0.0, 0
+    for blk in order:
+        rows = np.arange(blk * w.block, min((blk + 1) * w.block, w.n))
+        t0 = time.perf_counter()
+        A.attention(q, k, v, w.block, rp, ci, rows=rows)
+        t_used += time.perf_counter() - t0
+        sel = 0
+        ti = len(rows)
+        for j in ci[rp[blk]:rp[blk + 1]]:
+            sel += ti * min(w.block, w.n - int(j) * w.block) if j < blk else ti * (ti + 1) // 2
+        sel_pairs += sel
+        done_rows += ti
+        blocks += 1
+        if t_used >= target_s:
+            break
+    flops = 4.0 * w.d * w.batch * w.heads_q * sel_pairs
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{blocks} of {nqb} query blocks ({done_rows} query rows x {w.batch * w.heads_q} heads, "
+                      f"spread evenly over the sequence), fp64 masked-dense numpy, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path shards by "
+              f"(batch, kv-head) with no collective and is measured on one GPU's share).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_block_amd as bsa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = synth.make_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    od = torch.empty_like(qd)
+
+    spec = bsa.route_spec(w.route_kind, w.n_local, w.keep_first, w.n_random, w.route_seed)
+    nnz = bsa.bsa_build_route(spec, w.n, w.block)
+    rp = torch.empty(w.nqb + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(nnz, dtype=torch.int32, device=dev)
+    ws = torch.empty(bsa.bsa_dense_route_workspace_bytes(w.n, w.block) // 4, dtype=torch.int32, device=dev)
+    od_dense = torch.empty_like(qd)
+
+    def route_step():
+        bsa.bsa_build_route(spec, w.n, w.block, rp, ci)
+
+    def fwd():
+        bsa.bsa_forward(qd, kd, vd, od, rp, ci, w.block)
+
+    def step():
+        route_step()
+        fwd()
+
+    def dense():
+        bsa.bsa_dense_causal_ref(qd, kd, vd, od_dense, ws, w.block)
+
+    route_step()
+    torch.cuda.synchronize()
+    rp_h, ci_h = rp.cpu().numpy(), ci.cpu().numpy()
+    S = selected_pairs(rp_h, ci_h, w.n, w.block)
+    S_dense = w.n * (w.n + 1) // 2  # the dense causal route selects every causal pair
+    flops = 4.0 * w.d * w.batch * w.heads_q * S
+    flops_dense = 4.0 * w.d * w.batch * w.heads_q * S_dense
+
+    # the timed region: K steps (route build + forward)
+    ms_step = time_loop(step, args.steps, args.warmup)
+    # dominant kernel alone, and the dense baseline, in both orders
+    ms_fwd_a = time_loop(fwd, args.steps, 3)
+    ms_dense_a = time_loop(dense, max(5, args.steps // 4), 2)
+    ms_dense_b = time_loop(dense, max(5, args.steps // 4), 2)
+    ms_fwd_b = time_loop(fwd, args.steps, 3)
+    ms_route = time_loop(route_step, args.steps, 3)
+    fwd_samples = per_call_samples(fwd, max(20, args.steps))
+    ms_fwd = min(ms_fwd_a, ms_fwd_b)
+    ms_dense = min(ms_dense_a, ms_dense_b)
+
+    tflops_step = flops / (ms_step * 1e-3) / 1e12
+    tflops_fwd = flops / (ms_fwd * 1e-3) / 1e12
+    tflops_dense = flops_dense / (ms_dense * 1e-3) / 1e12
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            traffic = json.load(f).get("traffic")
+
+    out = {
+        "metric": "selected-interaction TFLOP/s (block-sparse attention forward, bf16 MFMA)",
+        "value": round(tflops_step, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V)",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "seq_len": w.n, "head_dim": w.d, "block": w.block,
+                   "route": {0: "bf1", 1: "block_diagonal", 2: "dense_causal", 3: "static_random"}[w.route_kind],
+                   "nnz": int(nnz), "selected_pairs_per_head": int(S)},
+        "pct_bf16_peak": round(100.0 * tflops_step / BF16_PEAK_TFLOPS, 2),
+        "forward_ms": round(ms_fwd, 5),
+        "forward_tflops": round(tflops_fwd, 2),
+        "forward_ms_median_p10_p90": [round(float(np.median(fwd_samples)), 5),
+                                      round(float(np.percentile(fwd_samples, 10)), 5),
+                                      round(float(np.percentile(fwd_samples, 90)), 5)],
+        "route_build_ms": round(ms_route, 5),
+        "dense_route_ms": round(ms_dense, 5),
+        "dense_route_tflops": round(tflops_dense, 2),
+        "dense_ms_orders": {"sparse_then_dense": round(ms_dense_a, 5), "dense_then_sparse": round(ms_dense_b, 5)},
+        "sparse_ms_orders": {"sparse_then_dense": round(ms_fwd_a, 5), "dense_then_sparse": round(ms_fwd_b, 5)},
+        "speedup_vs_dense": round(ms_dense / ms_fwd, 3),
+        "ideal_speedup_vs_dense": round(S_dense / S, 3),
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(tflops_fwd, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops_fwd / peak, 4), "traffic": traffic,
+                     "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * bsa.h — causal block-sparse attention forward (prefill) on AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A sequence of n tokens is cut into blocks of B tokens; block b holds
+ * tokens [b*B, min((b+1)*B, n)), and there are nqb = ceil(n/B) blocks ("Block Sparse
+ * Attention in LLMs", section 3 "Why block sparse?").  A route gives each query block i
+ * the list of key blocks it reads — the block mask M_B of "Block-Sparse Attention"
+ * ("Math Or Compute Schema"), kept as adjacency lists like the allowed_blocks dictionary
+ * of "Block Sparse Attention in LLMs" (section 6 "GPU implementation view").  Per head,
+ * the output is exact softmax attention restricted to the route, with the mask applied
+ * before the softmax so excluded pairs carry weight exactly zero:
+ *
+ *     O[t] = sum_s P[t,s] V[s],   P[t,.] = softmax_s( scale * Q[t].K[s]  over s in sel(t) )
+ *     sel(t) = { s : s <= t, s < n, floor(s/B) in R(floor(t/B)) }
+ *
+ * (per-head formula softmax(Q_i K_i^T / sqrt(d_k)) V_i of "Block-Sparse Attention",
+ * section "Math Or Compute Schema"; a query block reads itself causally: "BF1: A Causal
+ * Dyadic Sparse-Attention Retrofit ...", Method; "bsbr", Solution, mask M_in).
+ *
+ * Conventions shared by every call:
+ *  - All tensor and route pointers are DEVICE pointers owned by the caller (for example
+ *    allocated by PyTorch).  The library allocates and frees nothing and keeps no state
+ *    apart from a thread-local error string.
+ *  - All device work is enqueued asynchronously on the caller's `stream` (NULL = the
+ *    default stream); no call synchronises the device unless stated.
+ *  - Every call returns a bsa_status and never aborts, exits or throws.  Arguments are
+ *    validated on the host before any HIP call, so an invalid call does no device work.
+ *    A launch failure reported by the HIP runtime maps to BSA_ERR_DEVICE.
+ *    bsa_last_error() returns a human-readable detail for the last non-OK return on the
+ *    calling thread.
+ *  - Calls are re-entrant; concurrent calls on different streams are independent.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, negative size, heads_q % heads_kv != 0 */
+    BSA_ERR_UNSUPPORTED = 2,      /* valid but not implemented: head dim, block width or dtype */
+    BSA_ERR_BAD_ROUTE = 3,        /* route contents violate the CSR rules (bsa_check_route) */
+    BSA_ERR_CAPACITY = 4,         /* a caller buffer is too small */
+    BSA_ERR_DEVICE = 5            /* the HIP runtime reported an error */
+} bsa_status;
+
+typedef enum bsa_dtype {
+    BSA_BF16 = 0, /* bfloat16 inputs and output; fp32 accumulation; bf16 MFMA */
+    BSA_FP32 = 1  /* float32 inputs and output; fp32 arithmetic throughout */
+} bsa_dtype;
+
+typedef enum bsa_route_kind {
+    /* BF1 causal dyadic route ("BF1 ...", Method and section 3.1 "Causal dyadic block graph"):
+     * R(i) = {i} u {i-l : 1<=l<=n_local, i-l>=0} u {i-2^k : k>=0, 2^k<=i} u ({0} if keep_first). */
+    BSA_ROUTE_BF1 = 0,
+    /* BSBR within-chunk term ("bsbr", Solution, mask M_in): R(i) = {i}. */
+    BSA_ROUTE_BLOCK_DIAGONAL = 1,
+    /* Dense causal attention as a route: R(i) = {0, ..., i}. */
+    BSA_ROUTE_DENSE_CAUSAL = 2,
+    /* Static-random nonlocal graph (BF1's topology control, "BF1 ...", section 5 "Topology
+     * control"; seed 17 in section 8): R(0) = {0}; for i >= 1, R(i) = {i} u ({0} if keep_first)
+     * u T(i), where T(i) holds the m = min(n_random, #candidates) candidates j (1..i-1 when
+     * keep_first, else 0..i-1) with the smallest (h(seed,i,j), j), h(seed,i,j) =
+     * SM(seed ^ SM((i<<32)|j)), SM = first SplitMix64 output from a given state (Steele, Lea &
+     * Flood, OOPSLA 2014), all arithmetic on unsigned 64-bit words. */
+    BSA_ROUTE_STATIC_RANDOM = 3
+} bsa_route_kind;
+
+/* Route parameters.  Fields a kind does not use are ignored. */
+typedef struct bsa_route_spec {
+    int32_t kind;       /* bsa_route_kind */
+    int32_t n_local;    /* BF1: local predecessors (the BF1 summary uses 2); >= 0 */
+    int32_t keep_first; /* BF1, static-random: nonzero keeps block 0 in every row */
+    int32_t n_random;   /* static-random: drawn earlier blocks per row (14); >= 0 */
+    uint64_t seed;      /* static-random: graph seed (17) */
+} bsa_route_spec;
+
+/*
+ * bsa_build_route — write the CSR route for n tokens at block width `block`.
+ *
+ * Output (device, caller-owned):
+ *   row_ptr  int32[nqb+1]: row_ptr[0] = 0, row_ptr[i+1] - row_ptr[i] = |R(i)|.
+ *   col_idx  int32[nnz]:   row i's key blocks, strictly ascending, so the self block i is last.
+ * nnz is computed on the host (closed-form row counts) and written to *nnz_out (host pointer,
+ * required).  Size query: when row_ptr == NULL only *nnz_out is written and no device work is
+ * done.  Otherwise col_capacity (entries available at col_idx) must be >= nnz, else
+ * BSA_ERR_CAPACITY with *nnz_out still set; col_idx may be NULL only when nnz == 0.
+ * Requires n >= 0, block >= 1, nqb and nnz < 2^31.  n == 0 writes row_ptr[0] = 0 only.
+ * The fill runs as integer kernels on `stream` ("BF1 ...", section 4: topology/planning is
+ * timed apart from the attention kernel).
+ */
+bsa_status bsa_build_route(const bsa_route_spec* spec, int64_t n, int32_t block,
+                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                           int64_t* nnz_out, hipStream_t stream);
+
+/*
+ * bsa_forward — block-sparse attention forward over a CSR route (see the top of this file).
+ *
+ * Layout (device, caller-owned, contiguous, d innermost, 16-byte aligned base pointers):
+ *   q, o  [batch, heads_q,  n, d]   in `dtype`
+ *   k, v  [batch, heads_kv, n, d]   in `dtype`
+ *   lse   float32 [batch, heads_q, n] or NULL: natural-log log-sum-exp of the scaled,
+ *         selected scores of each query row.
+ * Grouped-query attention: query head h reads key/value head h / (heads_q / heads_kv).
+ * scale <= 0 selects 1/sqrt(d).
+ * Route (device): row_ptr int32[nqb+1], col_idx int32[nnz] with nqb = ceil(n/block), shared by
+ * every batch entry and head.  Rows are read as given; entries outside [0, i] are skipped and
+ * indices are clamped to [0, nnz] so a malformed route cannot make the kernel read out of
+ * bounds, but only routes accepted by bsa_check_route give defined results.  With the
+ * environment variable BSA_VALIDATE_ROUTE=1 the route is copied to the host and checked first
+ * (this synchronises `stream`).
+ * Supported: d in {64, 128}; block in {64, 128}; dtype BF16 or FP32; any n >= 0 (the last block
+ * may be partial; batch == 0 or n == 0 is a no-op).  BF16 output is rounded to nearest-even
+ * from fp32; the bf16 path rounds the softmax weights to bf16 before the PV product.
+ */
+bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                       int32_t block, bsa_dtype dtype, float scale,
+                       const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                       hipStream_t stream);
+
+/*
+ * bsa_dense_causal_ref — the same forward kernel over the dense causal route (row i reads
+ * 0..i): the dense baseline the BF1 summary measures its speedups against ("BF1 ...",
+ * Abstract; section 5 "Per-layer prefill scaling").  The route is built into the caller's
+ * device workspace, which must hold bsa_dense_route_workspace_bytes(n, block) bytes
+ * (int32[nqb+1] row_ptr followed by int32[nqb(nqb+1)/2] col_idx), else BSA_ERR_CAPACITY.
+ * Other arguments as for bsa_forward.
+ */
+bsa_status bsa_dense_causal_ref(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n,
+                                int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                                int32_t* route_workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Workspace bytes bsa_dense_causal_ref needs for n tokens at width block (0 on bad input). */
+size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block);
+
+/*
+ * bsa_check_route — validate a CSR route held in HOST memory: row_ptr[0] == 0, row_ptr
+ * non-decreasing, row_ptr[nqb] == nnz, and every row strictly ascending within [0, i] and
+ * ending with i (the self block is mandatory, so no row is empty).  BSA_OK or
+ * BSA_ERR_BAD_ROUTE (detail in bsa_last_error).  Pure host code.
+ */
+bsa_status bsa_check_route(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz);
+
+/* Static name of a status code. */
+const char* bsa_status_string(bsa_status s);
+
+/* Detail for the last non-OK return on the calling thread ("" if none). */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

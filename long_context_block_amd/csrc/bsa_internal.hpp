@@ -1,0 +1,66 @@
+// bsa_internal.hpp — declarations shared by the host library and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// Closed-form |R(i)| for every route kind (see bsa_route_kind in bsa.h for the sets).
+// Used by the host (nnz, capacity checks) and by the device row-pointer kernel.
+__host__ __device__ inline int floor_log2_u64(uint64_t x) { return 63 - __builtin_clzll(x); }
+__host__ __device__ inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+__host__ __device__ inline int64_t route_row_count(int kind, int64_t i, int n_local, int keep_first,
+                                                   int n_random) {
+    switch (kind) {
+    case BSA_ROUTE_BF1: {
+        if (i == 0) return 1;
+        // offsets: local {1..min(n_local,i)} u dyadic {2^k <= i}; offset i is block 0
+        const int64_t nl = n_local < i ? n_local : i;
+        int64_t offs = nl + floor_log2_u64((uint64_t)i) + 1;
+        if (nl >= 1) offs -= floor_log2_u64((uint64_t)nl) + 1;  // powers of two counted twice
+        const bool first_already = (i <= n_local) || is_pow2(i);
+        return 1 + offs + ((keep_first && !first_already) ? 1 : 0);
+    }
+    case BSA_ROUTE_BLOCK_DIAGONAL:
+        return 1;
+    case BSA_ROUTE_DENSE_CAUSAL:
+        return i + 1;
+    case BSA_ROUTE_STATIC_RANDOM: {
+        if (i == 0) return 1;
+        const int64_t ncand = keep_first ? i - 1 : i;
+        const int64_t m = n_random < ncand ? n_random : ncand;
+        return 1 + (keep_first ? 1 : 0) + m;
+    }
+    default:
+        return -1;
+    }
+}
+
+// Launchers (defined in the kernel translation units).  They only enqueue work and return
+// the hipError_t of the launch.
+hipError_t launch_route_build(const bsa_route_spec& spec, int64_t nqb, int32_t* row_ptr,
+                              int32_t* col_idx, hipStream_t stream);
+
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    int32_t batch, heads_q, heads_kv;
+    int32_t nqb;
+    int64_t n;
+    int64_t nnz;
+    float scale_log2;  // softmax scale * log2(e): scores are exponentiated with exp2
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, int d, int block, hipStream_t stream);
+
+}  // namespace bsa

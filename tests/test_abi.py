@@ -1,0 +1,163 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared symbol, validates
+arguments before any HIP call, and its host-side route logic (closed-form nnz, route checker)
+agrees with the oracle."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import long_context_block_amd as bsa
+from oracle import routes as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bsa.LIB_PATH), reason="libbsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_calls():
+    assert set(declared_functions()) == set(bsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = bsa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert bsa.bsa_status_string(0) == "BSA_OK"
+    assert bsa.bsa_status_string(4) == "BSA_ERR_CAPACITY"
+    assert bsa.bsa_status_string(99) == "BSA_ERR_UNKNOWN"
+
+
+def _raw_forward(**kw):
+    args = dict(q=16, k=16, v=16, o=16, lse=None, batch=1, hq=2, hkv=1, n=256, d=64, block=64, dtype=0,
+                scale=0.0, rp=16, ci=16, nnz=8, stream=None)
+    args.update(kw)
+    return bsa.lib().bsa_forward(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"],
+                                 args["hq"], args["hkv"], args["n"], args["d"], args["block"], args["dtype"],
+                                 args["scale"], args["rp"], args["ci"], args["nnz"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(n=-5), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(hkv=0), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(block=32), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(q=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(o=24), bsa.BSA_ERR_INVALID_ARGUMENT),      # misaligned
+    (dict(lse=18), bsa.BSA_ERR_INVALID_ARGUMENT),    # misaligned lse
+    (dict(rp=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(nnz=3), bsa.BSA_ERR_INVALID_ARGUMENT),     # fewer entries than blocks
+    (dict(scale=float("inf")), bsa.BSA_ERR_INVALID_ARGUMENT),
+])
+def test_forward_rejects_bad_arguments(kw, status):
+    assert _raw_forward(**kw) == status
+    assert bsa.bsa_last_error() != ""
+
+
+def test_forward_empty_inputs_are_noops():
+    # no device work, so this runs without a GPU
+    assert _raw_forward(n=0, q=None, k=None, v=None, o=None, rp=None, ci=None, nnz=0) == bsa.BSA_OK
+    assert _raw_forward(batch=0, q=None, k=None, v=None, o=None) == bsa.BSA_OK
+
+
+def test_dense_ref_rejects_small_workspace():
+    L = bsa.lib()
+    need = bsa.bsa_dense_route_workspace_bytes(4096, 64)
+    assert need == (65 + 64 * 65 // 2) * 4
+    st = L.bsa_dense_causal_ref(16, 16, 16, 16, None, 1, 1, 1, 4096, 64, 64, 0, 0.0, 16, need - 4, None)
+    assert st == bsa.BSA_ERR_CAPACITY
+    st = L.bsa_dense_causal_ref(16, 16, 16, 16, None, 1, 1, 1, 4096, 64, 64, 0, 0.0, None, need, None)
+    assert st == bsa.BSA_ERR_INVALID_ARGUMENT
+
+
+ROUTE_CASES = [
+    (R.BF1, dict(n_local=2, keep_first=1)), (R.BF1, dict(n_local=1, keep_first=1)),
+    (R.BF1, dict(n_local=0, keep_first=0)), (R.BF1, dict(n_local=5, keep_first=1)),
+    (R.BF1, dict(n_local=3, keep_first=0)),
+    (R.BLOCK_DIAGONAL, {}), (R.DENSE_CAUSAL, {}),
+    (R.STATIC_RANDOM, dict(n_random=14, keep_first=1)), (R.STATIC_RANDOM, dict(n_random=3, keep_first=0)),
+    (R.STATIC_RANDOM, dict(n_random=0, keep_first=1)),
+]
+
+
+@pytest.mark.parametrize("kind,params", ROUTE_CASES)
+@pytest.mark.parametrize("n,B", [(512, 64), (4096, 64), (8192, 128), (32768, 128), (1000, 64), (1, 64), (0, 64)])
+def test_route_size_query_matches_oracle(kind, params, n, B):
+    spec = bsa.route_spec(kind, params.get("n_local", 2), params.get("keep_first", 1),
+                          params.get("n_random", 14), 17)
+    nnz = bsa.bsa_build_route(spec, n, B)  # col_idx None: host-only size query
+    oparams = dict(n_local=params.get("n_local", 2), keep_first=bool(params.get("keep_first", 1)),
+                   n_random=params.get("n_random", 14), seed=17)
+    nqb = R.num_blocks(n, B)
+    if kind == R.STATIC_RANDOM and nqb > 600:
+        want = sum(min(params.get("n_random", 14), (i - 1 if params.get("keep_first", 1) else i)) +
+                   1 + (1 if params.get("keep_first", 1) else 0) if i > 0 else 1 for i in range(nqb))
+    else:
+        want = int(R.to_csr(R.route_sets(kind, nqb, **oparams))[0][-1])
+    assert nnz == want
+
+
+def test_route_spec_rejected():
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_build_route(bsa.route_spec(9), 100, 64)
+    assert e.value.status == bsa.BSA_ERR_INVALID_ARGUMENT
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_build_route(bsa.route_spec(0, n_local=-1), 100, 64)
+
+
+@pytest.mark.parametrize("kind", [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM])
+def test_check_route_accepts_oracle_routes(kind):
+    rp, ci = R.route_csr(kind, 3000, 64)
+    bsa.bsa_check_route(rp, ci)
+
+
+@pytest.mark.parametrize("mutate,msg", [
+    (lambda rp, ci: ci.__setitem__(3, 2), "outside"),          # row 2 reads block ... non-causal / order
+    (lambda rp, ci: ci.__setitem__(0, 1), "outside"),          # row 0 reads block 1
+    (lambda rp, ci: ci.__setitem__(slice(4, 6), ci[4:6][::-1].copy()), "ascending"),
+    (lambda rp, ci: rp.__setitem__(0, 1), "row_ptr[0]"),
+])
+def test_check_route_rejects_malformed(mutate, msg):
+    rp, ci = R.route_csr(R.BF1, 512, 64)
+    rp, ci = rp.copy(), ci.copy()
+    mutate(rp, ci)
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_check_route(rp, ci)
+    assert e.value.status == bsa.BSA_ERR_BAD_ROUTE
+
+
+def test_check_route_rejects_missing_self_and_empty_rows():
+    rp = np.array([0, 1, 2], dtype=np.int32)
+    ci = np.array([0, 0], dtype=np.int32)  # row 1 lacks block 1
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_check_route(rp, ci)
+    rp = np.array([0, 1, 1], dtype=np.int32)
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_check_route(rp, np.array([0], dtype=np.int32))
+    # the non-causal toy adjacency of "Block Sparse Attention in LLMs" (section 6) is rejected
+    rp = np.array([0, 2, 5, 8], dtype=np.int32)
+    ci = np.array([0, 1, 0, 1, 2, 1, 2, 3], dtype=np.int32)
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_check_route(rp, ci)
+
+
+def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(bsa, "LIB_PATH", str(tmp_path / "libbsa.so"))
+    monkeypatch.setattr(bsa, "_lib", None)
+    with pytest.raises(RuntimeError):
+        bsa.lib()
