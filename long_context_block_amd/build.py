@@ -26,10 +26,14 @@ ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-source extras.  fwd_bf16.hip keeps MFMA results in VGPRs: two wavefronts per SIMD, and the
+# rare rescale multiplies the accumulators in place instead of shuttling them through AGPRs.
+EXTRA_FLAGS = {
+    "fwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -45,7 +49,7 @@ def sources() -> list[str]:
 
 def _compile(hipcc: str, src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,6 +58,26 @@ def _compile(hipcc: str, src: str, verbose: bool) -> str:
     if verbose and r.stderr.strip():
         print(r.stderr, file=sys.stderr)
     return obj
+
+
+def check_m0(hipcc: str, src: str) -> None:
+    """The asynchronous LDS copy helper sets M0 in inline asm; M0 is reserved by the compiler and
+    cannot be declared clobbered, so the generated code must contain no other M0 user.  Compile
+    the device code to assembly and check that every M0 write is the helper's, immediately
+    followed by its global_load_lds_dwordx4, and that nothing else references M0."""
+    out = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".s")
+    cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "--cuda-device-only", "-S", src,
+           "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    lines = [ln.strip() for ln in open(out)]
+    for k, ln in enumerate(lines):
+        if ln.startswith(";") or "m0" not in ln.replace(",", " ").split():
+            continue
+        nxt = lines[k + 1] if k + 1 < len(lines) else ""
+        if not (ln.startswith("s_mov_b32 m0,") and nxt.startswith("global_load_lds_dwordx4")):
+            raise RuntimeError(f"{src}: unexpected M0 use in generated code: {ln!r}")
 
 
 def build(verbose: bool = False) -> str:
@@ -71,6 +95,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    for src in srcs:
+        if "copy16_to_lds" in open(src).read():
+            check_m0(hipcc, src)
     return LIB
 
 
