@@ -110,9 +110,10 @@ bsa_status bsa_build_route(const bsa_route_spec* spec, int64_t n, int32_t block,
  * Grouped-query attention: query head h reads key/value head h / (heads_q / heads_kv).
  * scale <= 0 selects 1/sqrt(d).
  * Route (device): row_ptr int32[nqb+1], col_idx int32[nnz] with nqb = ceil(n/block), shared by
- * every batch entry and head.  Rows are read as given; entries outside [0, i] are skipped and
- * indices are clamped to [0, nnz] so a malformed route cannot make the kernel read out of
- * bounds, but only routes accepted by bsa_check_route give defined results.  With the
+ * every batch entry and head.  Rows are read as given; row pointers are clamped to [0, nnz] and
+ * entries outside [0, i] are read as block i, so a malformed route cannot make the kernel read
+ * out of bounds, but only routes accepted by bsa_check_route give defined results (the bf16
+ * kernels take the last entry of a row as its diagonal block).  With the
  * environment variable BSA_VALIDATE_ROUTE=1 the route is copied to the host and checked first
  * (this synchronises `stream`).
  * Supported: d in {64, 128}; block in {64, 128}; dtype BF16 or FP32; any n >= 0 (the last block

@@ -33,6 +33,7 @@ HIPCC_FLAGS = [
 # rare rescale multiplies the accumulators in place instead of shuttling them through AGPRs.
 EXTRA_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "fwd_bf16_basic.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 

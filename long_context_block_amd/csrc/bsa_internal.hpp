@@ -61,6 +61,7 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream);
+hipError_t launch_fwd_bf16_basic(const FwdParams& p, int d, int block, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int block, hipStream_t stream);
 
 }  // namespace bsa

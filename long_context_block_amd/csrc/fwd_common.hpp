@@ -56,14 +56,34 @@ __device__ inline bf16x8 v_fragment(const __bf16* Vs, int vrow, int vcol) {
     return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
 }
 
-// Work item of a launch of `total` work-groups over head slices of nqb query blocks each:
-// longest rows (largest i) first, and consecutive work items of one head slice packed onto
-// one XCD (work-groups are dispatched round-robin over the 8 XCDs) so that they share K/V
-// tiles in that XCD's L2.
-__device__ inline void work_item(int64_t w, int64_t total, int64_t nqb, int64_t& slice, int64_t& i) {
-    const int64_t vi = (total % 8 == 0) ? (w % 8) * (total / 8) + w / 8 : w;
+// The same fragment read at a precomputed element address p of the first row (rows p and
+// p + 8 rows).
+template <int D>
+__device__ inline bf16x8 v_fragment_at(const __bf16* p) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * D));
+    const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+}
+
+// Work item k of work-group w in a persistent launch of G work-groups over `total` items
+// (head slices of nqb query blocks each).  Items are taken longest row first (largest i) within
+// a slice.  Work-groups are dispatched round-robin over the 8 XCDs, so when both counts allow it
+// the items are split into 8 contiguous ranges, one per XCD, and the work-groups of an XCD share
+// K/V tiles of the same heads in its L2; within a range, work-group c of C takes items in
+// serpentine order (c, 2C-1-c, 2C+c, ...), which evens out the row lengths.  Returns false
+// past the work-group's last item.
+__device__ inline bool work_item(int w, int G, int k, int total, int nqb, int& slice, int& i) {
+    const bool xcd = (total % 8 == 0) && (G % 8 == 0);
+    const int c = xcd ? w / 8 : w;
+    const int C = xcd ? G / 8 : G;
+    const int range = xcd ? total / 8 : total;
+    const int64_t pos = (int64_t)k * C + ((k & 1) ? C - 1 - c : c);
+    if (pos >= range) return false;
+    const int vi = (xcd ? (w % 8) * range : 0) + (int)pos;
     slice = vi / nqb;
     i = nqb - 1 - (vi % nqb);
+    return true;
 }
 
 }  // namespace fwd
@@ -87,6 +107,20 @@ __device__ inline void copy16_to_lds(const void* src, uint32_t lds_base) {
 }
 
 __device__ inline uint32_t lds_addr(const __bf16* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+
+// The same copy with a wavefront-uniform global base (scalar registers) and a per-lane 32-bit
+// byte offset: global_load_lds_dwordx4 in its scalar-base form, so a lane holds one offset
+// register instead of a 64-bit address.
+__device__ inline void copy16_to_lds(const void* base, uint32_t off, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    // readfirstlane works on (signed) int: widen each half as unsigned, never sign-extended
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t bu = (hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(off), "s"(bu)
+                 : "memory");
+}
 
 }  // namespace fwd
 }  // namespace bsa
