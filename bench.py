@@ -90,6 +90,20 @@ def per_call_samples(fn, reps: int):
     return np.array([a.elapsed_time(b) for a, b in evs])
 
 
+def gemm_reference(dev, size: int = 8192, reps: int = 20) -> dict:
+    """A plain bf16 GEMM through torch (hipBLASLt) on random N(0,1) operands, timed like the
+    forward: the matrix-core rate this GPU sustains under its power limit on realistic data,
+    reported beside the published dense peak for context."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(size, size, dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn(size, size, dtype=torch.bfloat16, device=dev, generator=g)
+    c = torch.empty(size, size, dtype=torch.bfloat16, device=dev)
+    ms = time_loop(lambda: torch.matmul(a, b, out=c), reps, 5)
+    return {"what": f"torch.matmul bf16 {size}x{size}x{size}, random N(0,1) operands",
+            "tflops": round(2.0 * size ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4)}
+
+
 def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
     """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload."""
     from oracle import attn as A
@@ -253,6 +267,8 @@ def main():
                      "peak": peak, "unit": "TFLOP/s", "frac": round(tflops_fwd / peak, 4), "traffic": traffic,
                      "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"},
     }
+    if w.dtype == "bf16":
+        out["roofline"]["gemm_reference"] = gemm_reference(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)
     print(json.dumps(out), flush=True)
