@@ -33,7 +33,11 @@
 //    P V product of step t-1 with the row max of step t, so the vector ALU and the matrix
 //    cores of a wavefront work at the same time (the other wavefront of the SIMD fills the
 //    remaining gaps).  The diagonal block, last in every valid row, runs unpipelined steps
-//    with the causal mask.
+//    with the causal mask; while it computes, the next item's Q is loaded into registers
+//    (the second score buffer is free then), so its latency is hidden.
+//  * Epilogue: O = acc / l rounded to bf16; one exchange between the half-wavefronts
+//    (v_permlane32_swap) gives every lane 8 consecutive columns, so each wavefront writes its
+//    32 rows with 16-byte stores.
 //  * Online softmax ("Block Sparse Attention in LLMs", section 7: tile, never materialise the
 //    n x n matrix) in the log2 domain with exp2.  A row's running max is only raised when a
 //    step's max exceeds it by more than kRescaleSlack (the final division by the running sum
@@ -154,7 +158,18 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
     };
 
     // ---- Q fragments (B operand of S^T = K Q^T): Q[row][16kk + 8hf .. +8] ------------------
-    bf16x8 qf[D / 16];
+    bf16x8 qf[D / 16], qn[D / 16];
+    auto load_q_into = [&](bf16x8 (&dst)[D / 16], const Item& it) {
+        const int64_t qrow = (int64_t)it.i * BLK + qloc;
+        const int64_t qr = qrow < n ? qrow : n - 1;
+        const __bf16* Qr = (const __bf16*)p.q + ((int64_t)it.head * n + qr) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) dst[kk] = *(const bf16x8*)(Qr + 16 * kk + 8 * hf);
+        if (qrow >= n) {
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) dst[kk] = bf16x8{};
+        }
+    };
     auto load_q = [&](const Item& it) {
         const int64_t qrow = (int64_t)it.i * BLK + qloc;
         const int64_t qr = qrow < n ? qrow : n - 1;
@@ -423,15 +438,18 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
                 barrier_chunk(NCH - 1);
                 // finish the pipeline (step (NCH-2, 1) waits in sB)
                 exp_pack(sB, pk);
+                // the score buffer sB is free until the next item: the next item's Q lands
+                // there while the diagonal block computes
+                if (nxt.ok) load_q_into(qn, nxt);
                 pv(sV[vst(NCH - 2)], KC, pk);
+            } else if (nxt.ok) {
+                load_q_into(qn, nxt);
             }
             simple_step(NCH - 1, 0);
             simple_step(NCH - 1, 1);
-            // the next item's Q
-            if (nxt.ok) load_q(nxt);
             gbase += NCH;
         } else if (nxt.ok) {
-            load_q(nxt);
+            load_q_into(qn, nxt);
         }
         pref = nxt_chunks;
         // this wavefront's copies of the next item's first chunk and its next Q have landed;
@@ -444,19 +462,34 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
         const int64_t qrow = (int64_t)cur.i * BLK + qloc;
         if (qrow < n) {
             __bf16* Or = (__bf16*)p.o + ((int64_t)cur.head * n + qrow) * D;
+            // A lane holds d = 32 db + 8 j4 + 4 hf + (0..3).  For a pair of j4 (2 jp, 2 jp + 1),
+            // one exchange between the half-wavefronts (v_permlane32_swap) gives lane (row, hf)
+            // the 8 consecutive d = 32 db + 16 jp + 8 hf + (0..7): one 16-byte store.
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int j4 = 0; j4 < 4; ++j4) {
-                    const int d0 = 32 * db + 8 * j4 + 4 * hf;
-                    const uint32_t w0 = pack_bf16x2(acc[db][4 * j4] * inv, acc[db][4 * j4 + 1] * inv);
-                    const uint32_t w1 = pack_bf16x2(acc[db][4 * j4 + 2] * inv, acc[db][4 * j4 + 3] * inv);
-                    *(uint2*)(Or + d0) = make_uint2(w0, w1);
+                for (int jp = 0; jp < 2; ++jp) {
+                    uint32_t x[2], y[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        x[h] = pack_bf16x2(acc[db][8 * jp + 2 * h] * inv, acc[db][8 * jp + 2 * h + 1] * inv);
+                        y[h] = pack_bf16x2(acc[db][8 * jp + 4 + 2 * h] * inv, acc[db][8 * jp + 4 + 2 * h + 1] * inv);
+                    }
+                    uint32_t lo[2], hi[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(x[h], y[h], false, false);
+                        lo[h] = sw[0];  // lanes < 32: own x; lanes >= 32: y of lane - 32
+                        hi[h] = sw[1];  // lanes < 32: x of lane + 32; lanes >= 32: own y
+                    }
+                    *(uint4*)(Or + 32 * db + 16 * jp + 8 * hf) = make_uint4(lo[0], lo[1], hi[0], hi[1]);
                 }
             if (p.lse && hf == 0) p.lse[(int64_t)cur.head * n + qrow] = (m_run + __log2f(lt)) * kLn2;
         }
         if (!nxt.ok) break;
         cur = nxt;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = qn[kk];
     }
 }
 
