@@ -2,6 +2,7 @@
 """Benchmark: causal block-sparse attention forward (prefill) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_32k] [--no-cpu-baseline]
+                    [--no-others]
 
 Workload (default): the Qwen3-0.6B-shaped layer at 32K tokens — batch 1, 16 query / 8 key-value
 heads, d = 128, block 128, bf16, BF1 route — the geometry the BF1 summary quotes its 32K
@@ -13,6 +14,11 @@ block-sparse forward over it.  W untimed warmup steps, then exactly K steps betw
 on the launch stream, bracketed by torch.cuda.synchronize().  Separately timed on the same
 inputs: the forward alone (the dominant kernel, for the roofline), and the same kernel over the
 dense causal route (the speedup denominator), in both orders sparse->dense and dense->sparse.
+
+Also reported, outside the timed region: the topology sweep (BF1 against the local sliding band
+and the static-random graph at the nearest selected-pair count, same inputs, with each graph's
+communication depth) and the forward alone on the other workloads, each against the roofline
+that bounds it (HBM bytes, matrix-core flops or vector flops).
 
 Prints ONE JSON line.  value = selected-interaction TFLOP/s of the step, where selected FLOPs =
 4 * d * batch * heads_q * S and S counts the causal token pairs the route selects (QK^T and PV
@@ -104,6 +110,134 @@ def gemm_reference(dev, size: int = 8192, reps: int = 20) -> dict:
             "tflops": round(2.0 * size ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4)}
 
 
+def graph_depth(row_ptr: np.ndarray, col_idx: np.ndarray) -> tuple[int, int]:
+    """Largest shortest-path hop count over ordered block pairs j < i, edges j -> i for j in R(i)
+    (the communication depth the BF1 summary compares topologies by, section 5), over the pairs
+    that are connected, and the number of pairs j < i with no path."""
+    from collections import deque
+    nqb = len(row_ptr) - 1
+    succ = [[] for _ in range(nqb)]
+    for i in range(nqb):
+        for j in col_idx[row_ptr[i]:row_ptr[i + 1]]:
+            if int(j) != i:
+                succ[int(j)].append(i)
+    worst, unreachable = 0, 0
+    for src in range(nqb):
+        dist = np.full(nqb, -1, dtype=np.int64)
+        dist[src] = 0
+        dq = deque([src])
+        while dq:
+            u = dq.popleft()
+            for x in succ[u]:
+                if dist[x] < 0:
+                    dist[x] = dist[u] + 1
+                    dq.append(x)
+        tail = dist[src + 1:]
+        unreachable += int((tail < 0).sum())
+        if len(tail):
+            worst = max(worst, int(tail.max()))
+    return worst, unreachable
+
+
+def topology_sweep(w, qd, kd, vd, steps: int) -> dict:
+    """BF1 against its two equal-budget controls on the same inputs ("BF1 ...", section 5
+    "Topology control": equal-pair-count BF1, sliding and static-random routes have nearly
+    identical sparse kernel time; "Communication depth"): the local sliding band and the
+    static-random graph whose parameter gives the selected-pair count nearest to BF1's."""
+    import torch
+    import long_context_block_amd as bsa
+    od = torch.empty_like(qd)
+
+    def build(kind, **kw):
+        spec = bsa.route_spec(kind, kw.get("n_local", w.n_local), w.keep_first, kw.get("n_random", w.n_random),
+                              w.route_seed)
+        rp, ci = bsa.build_route(spec, w.n, w.block)
+        torch.cuda.synchronize()
+        return rp, ci
+
+    def pairs(rp, ci):
+        return selected_pairs(rp.cpu().numpy(), ci.cpu().numpy(), w.n, w.block)
+
+    rp0, ci0 = build(bsa.BSA_ROUTE_BF1)
+    target = pairs(rp0, ci0)
+    best = {}
+    for kind, key in ((bsa.BSA_ROUTE_SLIDING_WINDOW, "n_local"), (bsa.BSA_ROUTE_STATIC_RANDOM, "n_random")):
+        cands = []
+        for val in range(0, 64):
+            rp, ci = build(kind, **{key: val})
+            cands.append((abs(pairs(rp, ci) - target), val))
+        best[kind] = (key, min(cands)[1])
+    out = {}
+    routes = [("bf1", bsa.BSA_ROUTE_BF1, {}),
+              ("sliding_window", bsa.BSA_ROUTE_SLIDING_WINDOW, {best[bsa.BSA_ROUTE_SLIDING_WINDOW][0]:
+                                                               best[bsa.BSA_ROUTE_SLIDING_WINDOW][1]}),
+              ("static_random", bsa.BSA_ROUTE_STATIC_RANDOM, {best[bsa.BSA_ROUTE_STATIC_RANDOM][0]:
+                                                             best[bsa.BSA_ROUTE_STATIC_RANDOM][1]})]
+    built = [(name, kw) + build(kind, **kw) for name, kind, kw in routes]
+    fns = [(lambda rp=rp, ci=ci: bsa.bsa_forward(qd, kd, vd, od, rp, ci, w.block)) for _, _, rp, ci in built]
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.3:  # steady clock before the sweep
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+    best_ms = [float("inf")] * len(fns)
+    for _ in range(3):  # interleaved rounds, best of three per route
+        for x, f in enumerate(fns):
+            best_ms[x] = min(best_ms[x], time_loop(f, steps, 3))
+    for (name, kw, rp, ci), ms in zip(built, best_ms):
+        S = pairs(rp, ci)
+        depth, unreachable = graph_depth(rp.cpu().numpy(), ci.cpu().numpy())
+        out[name] = {"params": kw, "nnz": int(ci.numel()), "selected_pairs_per_head": int(S),
+                     "forward_ms": round(ms, 5),
+                     "selected_tflops": round(4.0 * w.d * w.batch * w.heads_q * S / (ms * 1e-3) / 1e12, 2),
+                     "depth_hops": depth, "unreachable_block_pairs": unreachable}
+    return out
+
+
+def algorithmic_bytes(w) -> int:
+    """Q, K, V read once and O written once, in the workload's dtype."""
+    e = 4 if w.dtype == "fp32" else 2
+    return e * w.batch * w.n * w.d * (2 * w.heads_q + 2 * w.heads_kv)
+
+
+def other_workloads(names, steps: int) -> dict:
+    """The forward alone on the other workloads (parity cases of the same path), each against the
+    roofline that bounds it: HBM bytes for the streaming cases (bf1_4k, the block-diagonal
+    route), matrix-core flops for the 64K static-random graph, fp32 vector flops for the tiny
+    fp32 case (launch-latency bound in practice)."""
+    import torch
+    import long_context_block_amd as bsa
+    import synth
+    out = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        q, k, v = (x.cuda() for x in synth.make_qkv(w))
+        o = torch.empty_like(q)
+        rp, ci = bsa.build_route(bsa.route_spec(w.route_kind, w.n_local, w.keep_first, w.n_random, w.route_seed),
+                                 w.n, w.block)
+        S = selected_pairs(rp.cpu().numpy(), ci.cpu().numpy(), w.n, w.block)
+        fn = lambda: bsa.bsa_forward(q, k, v, o, rp, ci, w.block)  # noqa: E731
+        ms = time_loop(fn, max(10, steps), 5)
+        flops = 4.0 * w.d * w.batch * w.heads_q * S
+        nbytes = algorithmic_bytes(w)
+        tflops, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
+        if w.dtype == "fp32":
+            roof = {"bound": "alu", "achieved": round(tflops, 4), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 6)}
+        elif flops / nbytes < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
+        out[name] = {"forward_ms": round(ms, 5), "selected_tflops": round(tflops, 3),
+                     "algorithmic_bytes": nbytes, "algorithmic_GBs": round(gbs, 1), "nnz": int(ci.numel()),
+                     "roofline": roof}
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
     """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload."""
     from oracle import attn as A
@@ -142,6 +276,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads' forward timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="run only a plain device-to-device copy of MB MiB (calibrates rocprofv3 "
@@ -248,7 +383,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V)",
         "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "seq_len": w.n, "head_dim": w.d, "block": w.block,
-                   "route": {0: "bf1", 1: "block_diagonal", 2: "dense_causal", 3: "static_random"}[w.route_kind],
+                   "route": {0: "bf1", 1: "block_diagonal", 2: "dense_causal", 3: "static_random",
+                             4: "sliding_window"}[w.route_kind],
                    "nnz": int(nnz), "selected_pairs_per_head": int(S)},
         "pct_bf16_peak": round(100.0 * tflops_step / BF16_PEAK_TFLOPS, 2),
         "forward_ms": round(ms_fwd, 5),
@@ -269,6 +405,9 @@ def main():
     }
     if w.dtype == "bf16":
         out["roofline"]["gemm_reference"] = gemm_reference(dev)
+    if not args.no_others:
+        out["topology_sweep"] = topology_sweep(w, qd, kd, vd, args.steps)
+        out["other_workloads"] = other_workloads([x for x in synth.WORKLOADS if x != w.name], args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -69,13 +69,21 @@ typedef enum bsa_route_kind {
      * keep_first, else 0..i-1) with the smallest (h(seed,i,j), j), h(seed,i,j) =
      * SM(seed ^ SM((i<<32)|j)), SM = first SplitMix64 output from a given state (Steele, Lea &
      * Flood, OOPSLA 2014), all arithmetic on unsigned 64-bit words. */
-    BSA_ROUTE_STATIC_RANDOM = 3
+    BSA_ROUTE_STATIC_RANDOM = 3,
+    /* Local sliding band, BF1's equal-budget local control ("BF1 ...", Abstract; section 5
+     * "Topology control" and "Communication depth": matched sliding): the block and its
+     * n_local predecessors, R(i) = {j : max(0, i - n_local) <= j <= i}.  The fixed band of
+     * sliding-window attention, aligned to blocks ("Block-Sparse Attention", comparison with
+     * local and sliding-window attention).  n_local = 0 is the block-diagonal route and
+     * n_local >= nqb - 1 the dense causal route. */
+    BSA_ROUTE_SLIDING_WINDOW = 4
 } bsa_route_kind;
 
 /* Route parameters.  Fields a kind does not use are ignored. */
 typedef struct bsa_route_spec {
     int32_t kind;       /* bsa_route_kind */
-    int32_t n_local;    /* BF1: local predecessors (the BF1 summary uses 2); >= 0 */
+    int32_t n_local;    /* BF1: local predecessors (the BF1 summary uses 2); sliding: band
+                           predecessors (the window is n_local + 1 blocks); >= 0 */
     int32_t keep_first; /* BF1, static-random: nonzero keeps block 0 in every row */
     int32_t n_random;   /* static-random: drawn earlier blocks per row (14); >= 0 */
     uint64_t seed;      /* static-random: graph seed (17) */

@@ -30,6 +30,7 @@ BSA_ROUTE_BF1 = 0
 BSA_ROUTE_BLOCK_DIAGONAL = 1
 BSA_ROUTE_DENSE_CAUSAL = 2
 BSA_ROUTE_STATIC_RANDOM = 3
+BSA_ROUTE_SLIDING_WINDOW = 4
 
 EXPORTS = ("bsa_build_route", "bsa_forward", "bsa_dense_causal_ref", "bsa_dense_route_workspace_bytes",
            "bsa_check_route", "bsa_status_string", "bsa_last_error")

@@ -162,7 +162,7 @@ bsa_status bsa_build_route(const bsa_route_spec* spec, int64_t n, int32_t block,
                            int32_t* col_idx, int64_t col_capacity, int64_t* nnz_out, hipStream_t stream) {
     if (!spec || !nnz_out) return fail(BSA_ERR_INVALID_ARGUMENT, "spec and nnz_out must be non-NULL");
     if (n < 0 || block < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "need n >= 0 and block >= 1");
-    if (spec->kind < BSA_ROUTE_BF1 || spec->kind > BSA_ROUTE_STATIC_RANDOM)
+    if (spec->kind < BSA_ROUTE_BF1 || spec->kind > BSA_ROUTE_SLIDING_WINDOW)
         return fail(BSA_ERR_INVALID_ARGUMENT, "unknown route kind %d", spec->kind);
     if (spec->n_local < 0 || spec->n_random < 0)
         return fail(BSA_ERR_INVALID_ARGUMENT, "n_local and n_random must be >= 0");

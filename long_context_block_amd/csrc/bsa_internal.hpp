@@ -35,6 +35,8 @@ __host__ __device__ inline int64_t route_row_count(int kind, int64_t i, int n_lo
         const int64_t m = n_random < ncand ? n_random : ncand;
         return 1 + (keep_first ? 1 : 0) + m;
     }
+    case BSA_ROUTE_SLIDING_WINDOW:
+        return 1 + (n_local < i ? n_local : i);
     default:
         return -1;
     }

@@ -80,6 +80,11 @@ __global__ __launch_bounds__(64) void route_fill_kernel(bsa_route_spec spec, int
         for (int64_t j = lane; j <= i; j += 64) out[j] = (int32_t)j;
         return;
     }
+    if (spec.kind == BSA_ROUTE_SLIDING_WINDOW) {
+        const int64_t lo = i > spec.n_local ? i - spec.n_local : 0;
+        for (int64_t j = lo + lane; j <= i; j += 64) out[j - lo] = (int32_t)j;
+        return;
+    }
     if (spec.kind == BSA_ROUTE_BF1) {
         // Merge the descending offset lists {i (block 0)}, {2^k <= i}, {n_local..1} into
         // ascending block indices; the set is O(log i + n_local) long, so one lane does it.

@@ -4,9 +4,9 @@ This package is the plain, slow, obviously-correct definition of what the GPU
 path computes, written in numpy float64 from the source pages:
 
 * ``routes``  — the per-query-block key-block sets (BF1 causal dyadic route,
-  the BSBR within-chunk block-diagonal route, the dense causal route and a
-  seeded static-random nonlocal graph), their CSR encoding, and graph
-  properties (selected token pairs, shortest-path depth).
+  the BSBR within-chunk block-diagonal route, the dense causal route, a
+  seeded static-random nonlocal graph and the local sliding band), their CSR
+  encoding, and graph properties (selected token pairs, shortest-path depth).
 * ``attn``    — block-sparse attention as masked dense softmax attention:
   the route is expanded to an explicit token mask which is applied before the
   softmax, so excluded pairs get weight exactly zero.

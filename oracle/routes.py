@@ -30,6 +30,14 @@ Route kinds:
   ``(h(seed, i, j), j)`` where ``h`` is built from the SplitMix64 output
   function (Steele, Lea & Flood, "Fast splittable pseudorandom number
   generators", OOPSLA 2014).
+* Sliding window: BF1's equal-budget *local* control ("BF1 ...", Abstract:
+  equal-budget local sliding; section 5 "Topology control" and
+  "Communication depth": matched sliding).  Reading used here: a fixed band
+  aligned to blocks, the block itself and its ``n_local`` predecessors — the
+  fixed-band local pattern that "Block-Sparse Attention" compares against
+  (sliding-window attention), at block granularity.  The pages do not give
+  the band width of their matched control; a caller matches it to another
+  route's budget.
 
 Everything here is plain Python integers / sets; CSR conversion uses numpy.
 """
@@ -44,9 +52,11 @@ BF1 = 0
 BLOCK_DIAGONAL = 1
 DENSE_CAUSAL = 2
 STATIC_RANDOM = 3
+SLIDING_WINDOW = 4
 
 KIND_NAMES = {BF1: "bf1", BLOCK_DIAGONAL: "block_diagonal",
-              DENSE_CAUSAL: "dense_causal", STATIC_RANDOM: "static_random"}
+              DENSE_CAUSAL: "dense_causal", STATIC_RANDOM: "static_random",
+              SLIDING_WINDOW: "sliding_window"}
 
 _MASK64 = (1 << 64) - 1
 _GOLDEN_GAMMA = 0x9E3779B97F4A7C15
@@ -134,6 +144,11 @@ def static_random_set(i: int, n_random: int = 14, seed: int = 17,
     return s
 
 
+def sliding_window_set(i: int, n_local: int) -> set[int]:
+    """Local sliding band (BF1's equal-budget local control): blocks i-n_local .. i, clipped at 0."""
+    return {j for j in range(i - n_local, i + 1) if j >= 0}
+
+
 def route_sets(kind: int, nqb: int, n_local: int = 2, keep_first: bool = True,
                n_random: int = 14, seed: int = 17) -> list[list[int]]:
     """All rows R(0..nqb-1), each sorted ascending (so the self block is last)."""
@@ -147,6 +162,8 @@ def route_sets(kind: int, nqb: int, n_local: int = 2, keep_first: bool = True,
             s = dense_causal_set(i)
         elif kind == STATIC_RANDOM:
             s = static_random_set(i, n_random, seed, keep_first)
+        elif kind == SLIDING_WINDOW:
+            s = sliding_window_set(i, n_local)
         else:
             raise ValueError(f"unknown route kind {kind}")
         out.append(sorted(s))

@@ -25,6 +25,7 @@ ROUTE_BF1 = 0
 ROUTE_BLOCK_DIAGONAL = 1
 ROUTE_DENSE_CAUSAL = 2
 ROUTE_STATIC_RANDOM = 3
+ROUTE_SLIDING_WINDOW = 4
 
 
 @dataclass(frozen=True)

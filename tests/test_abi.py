@@ -92,6 +92,8 @@ ROUTE_CASES = [
     (R.BLOCK_DIAGONAL, {}), (R.DENSE_CAUSAL, {}),
     (R.STATIC_RANDOM, dict(n_random=14, keep_first=1)), (R.STATIC_RANDOM, dict(n_random=3, keep_first=0)),
     (R.STATIC_RANDOM, dict(n_random=0, keep_first=1)),
+    (R.SLIDING_WINDOW, dict(n_local=0)), (R.SLIDING_WINDOW, dict(n_local=8)),
+    (R.SLIDING_WINDOW, dict(n_local=100)),
 ]
 
 
@@ -120,7 +122,7 @@ def test_route_spec_rejected():
         bsa.bsa_build_route(bsa.route_spec(0, n_local=-1), 100, 64)
 
 
-@pytest.mark.parametrize("kind", [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM])
+@pytest.mark.parametrize("kind", [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM, R.SLIDING_WINDOW])
 def test_check_route_accepts_oracle_routes(kind):
     rp, ci = R.route_csr(kind, 3000, 64)
     bsa.bsa_check_route(rp, ci)

@@ -92,6 +92,9 @@ REDUCED = [
     synth.WORKLOADS["bf1_4k"].resized(name="gqa4-d64-b64", n=1100, d=64, heads_q=8, heads_kv=2),
     synth.WORKLOADS["bf1_4k"].resized(name="gqa3-d64-b128", n=900, d=64, block=128, heads_q=6, heads_kv=2),
     synth.WORKLOADS["bf1_4k"].resized(name="mqa-d128-b64", n=777, heads_q=4, heads_kv=1, batch=2),
+    synth.WORKLOADS["qwen3_32k"].resized(name="sliding-reduced", n=2100, route_kind=R.SLIDING_WINDOW, n_local=3),
+    synth.WORKLOADS["bf1_4k"].resized(name="sliding-d64-b64", n=1300, d=64, heads_q=4, heads_kv=4,
+                                      route_kind=R.SLIDING_WINDOW, n_local=5),
 ]
 
 
@@ -109,6 +112,14 @@ FULL = ["bsbr_chunk_8k", "qwen3_32k", "static_random_64k"]
 def test_parity_full_size_sampled(name):
     w = synth.WORKLOADS[name]
     rows = sample_rows(w.n, w.block, np.random.default_rng(7))
+    check(w, rows=rows)
+
+
+@pytest.mark.parametrize("kind,params", [(R.SLIDING_WINDOW, dict(n_local=8)), (R.STATIC_RANDOM, dict(n_random=7))])
+def test_parity_full_size_topology_controls_sampled(kind, params):
+    # the equal-budget controls of the topology sweep, at the 32K GQA shape
+    w = synth.WORKLOADS["qwen3_32k"].resized(route_kind=kind, **params)
+    rows = sample_rows(w.n, w.block, np.random.default_rng(9), extra=12)
     check(w, rows=rows)
 
 
@@ -152,7 +163,7 @@ def test_first_row_equals_v0():
 def test_uniform_weights_when_k_is_zero(dtype):
     # K = 0: every selected weight is exactly equal, so O[t] is the mean of V over sel(t); with
     # V[:, 0] = 1, V[:, 1] = s/n, V[:, 2] = (s/n)^2 this pins which tokens the kernel selects.
-    for kind in (R.BF1, R.STATIC_RANDOM, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL):
+    for kind in (R.BF1, R.STATIC_RANDOM, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.SLIDING_WINDOW):
         w = synth.WORKLOADS["bf1_4k"].resized(n=777, heads_q=1, heads_kv=1, d=64, dtype=dtype, route_kind=kind)
         dt = w.torch_dtype
         q = torch.randn(1, 1, w.n, 64).to(dt)

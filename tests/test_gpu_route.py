@@ -43,6 +43,8 @@ SWEEP = [
     (R.STATIC_RANDOM, dict(n_random=5, keep_first=0, seed=3)),
     (R.STATIC_RANDOM, dict(n_random=70, keep_first=1, seed=12345678901234)),
     (R.STATIC_RANDOM, dict(n_random=0, keep_first=1, seed=17)),
+    (R.SLIDING_WINDOW, dict(n_local=0)), (R.SLIDING_WINDOW, dict(n_local=8)),
+    (R.SLIDING_WINDOW, dict(n_local=70)),
 ]
 
 

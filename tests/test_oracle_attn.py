@@ -17,7 +17,7 @@ import torch.nn.functional as F
 from oracle import attn as A
 from oracle import routes as R
 
-KINDS = [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM]
+KINDS = [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM, R.SLIDING_WINDOW]
 
 
 def _qkv(b, hq, hkv, n, d, seed=0, dtype=torch.float64):
@@ -41,6 +41,8 @@ def _member(kind, i, j, nl=2):
         return i == j
     if kind == R.DENSE_CAUSAL:
         return 0 <= j <= i
+    if kind == R.SLIDING_WINDOW:
+        return 0 <= i - j <= nl
     return j in R.static_random_set(i, 14, 17, True)
 
 
@@ -58,6 +60,20 @@ def test_explicit_scale_matches_sdpa():
     rp, ci = R.route_csr(R.DENSE_CAUSAL, 64, 16)
     got = A.attention(q, k, v, 16, rp, ci, scale=0.3)
     ref = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=0.3).numpy()
+    assert np.abs(got - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("n,B,nl", [(256, 32, 2), (100, 16, 3), (64, 8, 0)])
+def test_sliding_window_is_banded_sdpa(n, B, nl):
+    # the library routine with an explicit boolean mask: key block within nl blocks before the
+    # query block, and causal
+    q, k, v = _qkv(2, 2, 1, n, 16, seed=11)
+    rp, ci = R.route_csr(R.SLIDING_WINDOW, n, B, n_local=nl)
+    got = A.attention(q, k, v, B, rp, ci)
+    t = torch.arange(n)
+    band = ((t[:, None] // B) - (t[None, :] // B) <= nl) & (t[None, :] <= t[:, None])
+    kk, vv = k.repeat_interleave(2, 1), v.repeat_interleave(2, 1)
+    ref = F.scaled_dot_product_attention(q, kk, vv, attn_mask=band).numpy()
     assert np.abs(got - ref).max() < 1e-12
 
 

@@ -165,3 +165,41 @@ def test_csr_roundtrip_and_partial_block():
     rp, ci = R.route_csr(R.BF1, n, B)
     assert len(rp) == R.num_blocks(n, B) + 1 == 6
     assert R.csr_to_sets(rp, ci) == R.route_sets(R.BF1, 5)
+
+
+# --- local sliding band (BF1's equal-budget local control) ---------------------------------
+
+@pytest.mark.parametrize("n_local", [0, 1, 3, 8])
+def test_sliding_window_closed_forms(n_local):
+    nqb = 200
+    sets = R.route_sets(R.SLIDING_WINDOW, nqb, n_local=n_local)
+    # membership predicate, written independently: 0 <= i - j <= n_local
+    for i in range(nqb):
+        assert sets[i] == [j for j in range(nqb) if 0 <= i - j <= n_local]
+    # nnz = sum_i min(i + 1, n_local + 1) = W * nqb - W (W - 1) / 2 for W = n_local + 1 <= nqb
+    W = n_local + 1
+    rp, ci = R.to_csr(sets)
+    assert rp[-1] == len(ci) == W * nqb - W * (W - 1) // 2
+
+
+def test_sliding_window_degenerate_cases():
+    nqb = 50
+    assert R.route_sets(R.SLIDING_WINDOW, nqb, n_local=0) == R.route_sets(R.BLOCK_DIAGONAL, nqb)
+    assert R.route_sets(R.SLIDING_WINDOW, nqb, n_local=nqb - 1) == R.route_sets(R.DENSE_CAUSAL, nqb)
+    assert R.route_sets(R.SLIDING_WINDOW, nqb, n_local=10 * nqb) == R.route_sets(R.DENSE_CAUSAL, nqb)
+
+
+@pytest.mark.parametrize("nqb,n_local", [(8, 1), (64, 2), (256, 8), (100, 7)])
+def test_sliding_window_depth_closed_form(nqb, n_local):
+    # a hop moves at most n_local blocks forward, and n_local-sized hops are always available:
+    # the worst pair (0, nqb - 1) needs ceil((nqb - 1) / n_local) hops
+    want = -(-(nqb - 1) // n_local)
+    assert R.max_shortest_path(R.route_sets(R.SLIDING_WINDOW, nqb, n_local=n_local)) == want
+
+
+def test_sliding_window_selected_pairs_closed_form():
+    # full blocks of B tokens: a row with k off-diagonal blocks selects k B^2 + B (B + 1) / 2
+    n, B, nl = 64 * 16, 16, 5
+    nqb = n // B
+    want = sum(min(i, nl) * B * B + B * (B + 1) // 2 for i in range(nqb))
+    assert R.selected_pairs(n, B, R.route_sets(R.SLIDING_WINDOW, nqb, n_local=nl)) == want
