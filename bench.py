@@ -15,7 +15,9 @@ on the launch stream, bracketed by torch.cuda.synchronize().  Separately timed o
 inputs: the forward alone (the dominant kernel, for the roofline), and the same kernel over the
 dense causal route (the speedup denominator), in both orders sparse->dense and dense->sparse.
 
-Also reported, outside the timed region: the topology sweep (BF1 against the local sliding band
+Also reported, outside the timed region: selected-page decode of the newest token over the same
+tensors as a key/value cache (batch 1 and 16; persistent plan, plan per token, dense route), the
+topology sweep (BF1 against the local sliding band
 and the static-random graph at the nearest selected-pair count, same inputs, with each graph's
 communication depth) and the forward alone on the other workloads, each against the roofline
 that bounds it (HBM bytes, matrix-core flops or vector flops).
@@ -191,6 +193,48 @@ def topology_sweep(w, qd, kd, vd, steps: int) -> dict:
                      "forward_ms": round(ms, 5),
                      "selected_tflops": round(4.0 * w.d * w.batch * w.heads_q * S / (ms * 1e-3) / 1e12, 2),
                      "depth_hops": depth, "unreachable_block_pairs": unreachable}
+    return out
+
+
+def decode_bench(w, kd, vd, steps: int, batch: int = 1) -> dict:
+    """Selected-page decode on the workload's key/value tensors as a cache (newest token at the
+    last position): with the route built once for the cache (persistent plan), with the plan
+    rebuilt for every token (the pages' per-token accounting, "BF1 ...", section 5), and over
+    the dense causal route (the speedup denominator).  Algorithmic bytes: the selected key and
+    value rows, q and o."""
+    import torch
+    import long_context_block_amd as bsa
+    hq, d = w.heads_q, w.d
+    e = 2 if w.dtype == "bf16" else 4
+    g = torch.Generator(device=kd.device).manual_seed(7)
+    q = torch.randn(batch, hq, d, device=kd.device, generator=g).to(kd.dtype)
+    kc = kd.expand(batch, -1, -1, -1).contiguous() if batch > 1 else kd
+    vc = vd.expand(batch, -1, -1, -1).contiguous() if batch > 1 else vd
+    o = torch.empty_like(q)
+    ws = torch.empty(bsa.bsa_decode_workspace_bytes(batch, hq, d) // 4, dtype=torch.float32, device=kd.device)
+    sl = torch.full((batch,), w.n, dtype=torch.int32, device=kd.device)
+    out = {"batch": batch, "token": w.n - 1}
+    for name, kind in (("bf1", w.route_kind), ("dense_causal", bsa.BSA_ROUTE_DENSE_CAUSAL)):
+        spec = bsa.route_spec(kind, w.n_local, w.keep_first, w.n_random, w.route_seed)
+        rp, ci = bsa.build_route(spec, w.n, w.block)
+        torch.cuda.synchronize()
+        rph, cih = rp.cpu().numpy(), ci.cpu().numpy()
+        i = (w.n - 1) // w.block
+        sel = sum(min(w.block, w.n - int(j) * w.block) for j in cih[rph[i]:rph[i + 1]])
+        nbytes = batch * (2 * w.heads_kv * sel * d * e + 2 * hq * d * e)
+        fn = lambda: bsa.bsa_decode(q, kc, vc, o, sl, rp, ci, w.block, ws)  # noqa: E731
+        ms = time_loop(fn, max(50, steps), 10)
+        rec = {"selected_keys": int(sel), "ms": round(ms, 5), "algorithmic_bytes": int(nbytes),
+               "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        if name == "bf1":
+            def planned():
+                bsa.bsa_build_route(spec, w.n, w.block, rp, ci)
+                fn()
+            rec["ms_with_plan_per_token"] = round(time_loop(planned, max(50, steps), 10), 5)
+        out[name] = rec
+    out["speedup_vs_dense"] = round(out["dense_causal"]["ms"] / out["bf1"]["ms"], 3)
     return out
 
 
@@ -407,6 +451,7 @@ def main():
         out["roofline"]["gemm_reference"] = gemm_reference(dev)
     if not args.no_others:
         out["topology_sweep"] = topology_sweep(w, qd, kd, vd, args.steps)
+        out["decode"] = [decode_bench(w, kd, vd, args.steps, batch) for batch in (1, 16)]
         out["other_workloads"] = other_workloads([x for x in synth.WORKLOADS if x != w.name], args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)

@@ -152,6 +152,39 @@ bsa_status bsa_dense_causal_ref(const void* q, const void* k, const void* v, voi
 size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block);
 
 /*
+ * bsa_decode — selected-page decode: one new query token per sequence against the key/value
+ * blocks of its route row ("BF1 ...", section 5 "Selected-page decode characterization"; the
+ * "decode-reference agreement" gate of section 4).  Sequence b holds seq_lens[b] tokens in its
+ * cache; its newest token t = seq_lens[b] - 1 (query block i = t / block) attends to the keys
+ * s <= t with floor(s / block) in R(i):
+ *
+ *     o[b, h] = sum_s P[s] v_cache[b, h/G, s],  P = softmax_s( scale * q[b, h] . k_cache[b, h/G, s] )
+ *
+ * which is row t of bsa_forward's output for that token (G = heads_q / heads_kv).
+ *
+ * Layout (device, caller-owned, contiguous, 16-byte aligned):
+ *   q, o              [batch, heads_q, d]          in `dtype`
+ *   k_cache, v_cache  [batch, heads_kv, n_max, d]  in `dtype` (rows >= seq_lens[b] are not read)
+ *   lse               float32 [batch, heads_q] or NULL (natural log)
+ *   seq_lens          int32 [batch] on the device; values are clamped to [1, n_max]
+ *   row_ptr, col_idx  the CSR route for n_max tokens at width `block` (as for bsa_forward):
+ *                     built once for the cache capacity, it serves every length up to n_max
+ *   workspace         float32 partials, at least bsa_decode_workspace_bytes(batch, heads_q, d)
+ *                     bytes, else BSA_ERR_CAPACITY; its contents on entry do not matter
+ * scale <= 0 selects 1/sqrt(d).  Supported: d in {64, 128}; block in {64, 128}; dtype BF16 or
+ * FP32; n_max >= 1; batch == 0 is a no-op.  fp32 arithmetic throughout (the softmax weights are
+ * not rounded); the output is rounded once to `dtype`.  Two kernels on `stream`.
+ */
+bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                      int64_t n_max, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                      const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                      float* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes bsa_decode needs (0 on bad input). */
+size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d);
+
+/*
  * bsa_check_route — validate a CSR route held in HOST memory: row_ptr[0] == 0, row_ptr
  * non-decreasing, row_ptr[nqb] == nnz, and every row strictly ascending within [0, i] and
  * ending with i (the self block is mandatory, so no row is empty).  BSA_OK or

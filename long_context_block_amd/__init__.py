@@ -33,7 +33,7 @@ BSA_ROUTE_STATIC_RANDOM = 3
 BSA_ROUTE_SLIDING_WINDOW = 4
 
 EXPORTS = ("bsa_build_route", "bsa_forward", "bsa_dense_causal_ref", "bsa_dense_route_workspace_bytes",
-           "bsa_check_route", "bsa_status_string", "bsa_last_error")
+           "bsa_decode", "bsa_decode_workspace_bytes", "bsa_check_route", "bsa_status_string", "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.bsa_dense_causal_ref.restype = ctypes.c_int
         L.bsa_dense_route_workspace_bytes.argtypes = [i64, i32]
         L.bsa_dense_route_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, ctypes.c_int, f32, vp, vp,
+                                 i64, vp, ctypes.c_size_t, vp]
+        L.bsa_decode.restype = ctypes.c_int
+        L.bsa_decode_workspace_bytes.argtypes = [i32, i32, i32]
+        L.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_check_route.argtypes = [vp, vp, i64, i64]
         L.bsa_check_route.restype = ctypes.c_int
         L.bsa_status_string.argtypes = [ctypes.c_int]
@@ -192,6 +197,37 @@ def bsa_dense_causal_ref(q, k, v, o, workspace, block: int, scale: float = 0.0, 
                                       workspace.numel() * 4, _stream(stream)))
 
 
+def bsa_decode_workspace_bytes(batch: int, heads_q: int, d: int) -> int:
+    return int(lib().bsa_decode_workspace_bytes(batch, heads_q, d))
+
+
+def bsa_decode(q, k_cache, v_cache, o, seq_lens, row_ptr, col_idx, block: int, workspace, scale: float = 0.0,
+               lse=None, stream=None) -> None:
+    """o[b, h] = attention of the newest token t = seq_lens[b] - 1 over its route row; q,o [b,Hq,d],
+    k_cache,v_cache [b,Hkv,n_max,d], seq_lens int32 [b] (GPU), workspace float32 (GPU)."""
+    import torch
+    dt = _dtype_code(q)
+    b, hq, d = q.shape
+    hkv, n_max = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (b, hkv, n_max, d) or tuple(v_cache.shape) != (b, hkv, n_max, d) or \
+            tuple(o.shape) != (b, hq, d):
+        raise ValueError("shape mismatch between q, k_cache, v_cache and o")
+    if tuple(seq_lens.shape) != (b,):
+        raise ValueError("seq_lens must have shape [b]")
+    if row_ptr.numel() != -(-n_max // block) + 1:
+        raise ValueError("row_ptr must hold the route for n_max tokens (ceil(n_max / block) + 1 entries)")
+    ptrs = [_dev_ptr(x, nm, q.dtype) for x, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (o, "o"))]
+    if lse is not None and tuple(lse.shape) != (b, hq):
+        raise ValueError("lse must have shape [b, Hq]")
+    lp = _dev_ptr(lse, "lse", torch.float32, allow_none=True)
+    sp = _dev_ptr(seq_lens, "seq_lens", torch.int32)
+    rp = _dev_ptr(row_ptr, "row_ptr", torch.int32)
+    ci = _dev_ptr(col_idx, "col_idx", torch.int32)
+    wp = _dev_ptr(workspace, "workspace", torch.float32)
+    _check(lib().bsa_decode(*ptrs, lp, sp, b, hq, hkv, n_max, d, block, dt, float(scale), rp, ci, col_idx.numel(),
+                            wp, workspace.numel() * 4, _stream(stream)))
+
+
 def bsa_check_route(row_ptr, col_idx) -> None:
     """Validate a CSR route held in host memory (numpy int32 arrays); raises BsaError if malformed."""
     import numpy as np
@@ -211,6 +247,18 @@ def build_route(spec: bsa_route_spec, n: int, block: int, device="cuda", stream=
     col_idx = torch.empty(max(nnz, 1), dtype=torch.int32, device=device)[:nnz]
     bsa_build_route(spec, n, block, row_ptr, col_idx, stream)
     return row_ptr, col_idx
+
+
+def decode(q, k_cache, v_cache, seq_lens, row_ptr, col_idx, block: int, scale: float = 0.0,
+           with_lse: bool = False, stream=None):
+    """Allocate the output, LSE and workspace and run bsa_decode."""
+    import torch
+    b, hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(b, hq, dtype=torch.float32, device=q.device) if with_lse else None
+    ws = torch.empty(max(1, bsa_decode_workspace_bytes(b, hq, d) // 4), dtype=torch.float32, device=q.device)
+    bsa_decode(q, k_cache, v_cache, o, seq_lens, row_ptr, col_idx, block, ws, scale, lse, stream)
+    return (o, lse) if with_lse else o
 
 
 def forward(q, k, v, row_ptr, col_idx, block: int, scale: float = 0.0, with_lse: bool = False, stream=None):

@@ -205,6 +205,66 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, flo
                        nnz, stream);
 }
 
+size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d) {
+    if (batch < 0 || heads_q < 1 || d < 1) return 0;
+    return (size_t)batch * heads_q * bsa::kDecodeMaxSplits * (d + 2) * sizeof(float);
+}
+
+bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n_max,
+                      int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
+                      const int32_t* col_idx, int64_t nnz, float* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || n_max < 1 || block < 1 || d < 1)
+        return fail(BSA_ERR_INVALID_ARGUMENT,
+                    "sizes must satisfy batch >= 0, heads >= 1, n_max >= 1, d >= 1, block >= 1 "
+                    "(got batch=%d heads_q=%d heads_kv=%d n_max=%lld d=%d block=%d)",
+                    batch, heads_q, heads_kv, (long long)n_max, d, block);
+    if (heads_q % heads_kv != 0)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+    if (dtype != BSA_BF16 && dtype != BSA_FP32) return fail(BSA_ERR_UNSUPPORTED, "dtype %d not supported", (int)dtype);
+    if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim d=%d not supported (64 or 128)", d);
+    if (block != 64 && block != 128) return fail(BSA_ERR_UNSUPPORTED, "block=%d not supported (64 or 128)", block);
+    if (!(scale <= 0.f) && !std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    const int64_t nqb = (n_max + block - 1) / block;
+    if (nqb > INT32_MAX - 1) return fail(BSA_ERR_UNSUPPORTED, "too many blocks (%lld)", (long long)nqb);
+    if (batch == 0) return ok();
+    if (!q || !k_cache || !v_cache || !o || !seq_lens || !row_ptr || !col_idx || !workspace)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o, seq_lens, route and workspace must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o and workspace must be 16-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    if (((uintptr_t)seq_lens & 3u) != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
+    if (nnz < nqb || nnz > INT32_MAX)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "nnz=%lld must be in [nqb=%lld, 2^31)", (long long)nnz, (long long)nqb);
+    const size_t need = bsa_decode_workspace_bytes(batch, heads_q, d);
+    if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
+
+    bsa::DecodeParams p;
+    p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
+    p.seq_lens = seq_lens; p.row_ptr = row_ptr; p.col_idx = col_idx; p.ws = workspace;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.block = block;
+    p.n_max = n_max; p.nnz = nnz;
+    const int G = heads_q / heads_kv;
+    p.gc = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    p.hchunks = G / p.gc;
+    // Splits: enough single-wavefront units to cover the device (~1024), but no more than the
+    // 32-key sub-blocks of an average row (the rows of these routes are of similar length).
+    const int64_t base_units = (int64_t)batch * heads_kv * p.hchunks;
+    const int64_t avg_sub = ((nnz + nqb - 1) / nqb) * (block / 32);
+    int64_t S = (1024 + base_units - 1) / base_units;
+    S = S < avg_sub ? S : avg_sub;
+    S = S < 1 ? 1 : (S > bsa::kDecodeMaxSplits ? bsa::kDecodeMaxSplits : S);
+    p.splits = (int32_t)S;
+    if (base_units * S > INT32_MAX || (int64_t)batch * heads_q > INT32_MAX)
+        return fail(BSA_ERR_UNSUPPORTED, "grid too large");
+    const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
+    p.scale_log2 = (float)(sc * 1.4426950408889634073599);
+    const hipError_t e = bsa::launch_decode(p, d, dtype == BSA_BF16, stream);
+    if (e != hipSuccess) return device_error(e, "decode launch");
+    return ok();
+}
+
 size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block) {
     if (n < 0 || block < 1) return 0;
     const int64_t nqb = (n + block - 1) / block;

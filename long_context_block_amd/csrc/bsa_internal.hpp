@@ -62,7 +62,28 @@ struct FwdParams {
     float scale_log2;  // softmax scale * log2(e): scores are exponentiated with exp2
 };
 
+struct DecodeParams {
+    const void* q;  // [batch, heads_q, d]
+    const void* k;  // [batch, heads_kv, n_max, d]
+    const void* v;
+    void* o;        // [batch, heads_q, d]
+    float* lse;     // [batch, heads_q] or null
+    const int32_t* seq_lens;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    float* ws;      // [batch, heads_q, splits, d + 2] partials
+    int32_t batch, heads_q, heads_kv, block;
+    int32_t splits;   // split units per (b, kv head, head group), <= kDecodeMaxSplits
+    int32_t hchunks;  // query-head groups per kv head
+    int32_t gc;       // query heads per group (1, 2, 4)
+    int64_t n_max;
+    int64_t nnz;
+    float scale_log2;
+};
+constexpr int kDecodeMaxSplits = 64;
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t stream);
 hipError_t launch_fwd_bf16_basic(const FwdParams& p, int d, int block, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int block, hipStream_t stream);
 

@@ -109,3 +109,38 @@ def attention_probs(q, k, B: int, row_ptr, col_idx, scale: float | None = None):
             E = np.exp(S - S.max(axis=1, keepdims=True))
             P[bi, h] = E / E.sum(axis=1, keepdims=True)
     return P
+
+
+def decode_attention(q, k_cache, v_cache, seq_lens, B: int, row_ptr, col_idx, scale: float | None = None,
+                     return_lse: bool = False):
+    """Selected-page decode, fp64: the newest token of each sequence against its route row.
+
+    Follows "BF1 ...", section 5 ("Selected-page decode characterization"): sequence b holds
+    ``seq_lens[b]`` cached tokens; its newest token t = seq_lens[b] - 1 (query block
+    i = t // B) attends to the cached keys s <= t whose block is in R(i), the row of the same
+    route the prefill uses — so the result is the prefill's row t ("decode-reference
+    agreement", section 4).  Lengths are clamped to [1, n_max].
+
+    q: [batch, Hq, d]; k_cache, v_cache: [batch, Hkv, n_max, d].
+    Returns o [batch, Hq, d] float64 (and LSE [batch, Hq], natural log, when ``return_lse``).
+    """
+    Q, K, V = _to_f64(q), _to_f64(k_cache), _to_f64(v_cache)
+    b, hq, d = Q.shape
+    hkv, n_max = K.shape[1], K.shape[2]
+    G = hq // hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    lens = np.clip(np.asarray(seq_lens, dtype=np.int64), 1, n_max)
+    out = np.empty((b, hq, d))
+    lse = np.empty((b, hq))
+    for bi in range(b):
+        t = int(lens[bi]) - 1
+        M = token_mask(n_max, B, row_ptr, col_idx, [t])[0]
+        for h in range(hq):
+            S = np.where(M, (K[bi, h // G] @ Q[bi, h]) * scale, -np.inf)
+            mx = S.max()
+            E = np.exp(S - mx)
+            den = E.sum()
+            out[bi, h] = (E / den) @ V[bi, h // G]
+            lse[bi, h] = mx + np.log(den)
+    return (out, lse) if return_lse else out

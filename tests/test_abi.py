@@ -75,6 +75,42 @@ def test_forward_empty_inputs_are_noops():
     assert _raw_forward(batch=0, q=None, k=None, v=None, o=None) == bsa.BSA_OK
 
 
+def _raw_decode(**kw):
+    args = dict(q=16, k=16, v=16, o=16, lse=None, sl=16, batch=2, hq=4, hkv=2, n_max=1000, d=128, block=128,
+                dtype=0, scale=0.0, rp=16, ci=16, nnz=8, ws=16, wsb=None, stream=None)
+    args.update(kw)
+    if args["wsb"] is None:
+        args["wsb"] = bsa.bsa_decode_workspace_bytes(args["batch"], args["hq"], args["d"])
+    return bsa.lib().bsa_decode(args["q"], args["k"], args["v"], args["o"], args["lse"], args["sl"], args["batch"],
+                                args["hq"], args["hkv"], args["n_max"], args["d"], args["block"], args["dtype"],
+                                args["scale"], args["rp"], args["ci"], args["nnz"], args["ws"], args["wsb"],
+                                args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(n_max=0), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(d=96), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(block=32), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(dtype=7), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(sl=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(q=24), bsa.BSA_ERR_INVALID_ARGUMENT),      # misaligned
+    (dict(nnz=7), bsa.BSA_ERR_INVALID_ARGUMENT),     # fewer entries than blocks (8)
+    (dict(wsb=100), bsa.BSA_ERR_CAPACITY),
+    (dict(scale=float("nan")), bsa.BSA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    assert _raw_decode(**kw) == status
+    assert bsa.bsa_last_error() != ""
+
+
+def test_decode_workspace_and_empty_batch():
+    assert bsa.bsa_decode_workspace_bytes(3, 16, 128) == 3 * 16 * 64 * 130 * 4
+    assert bsa.bsa_decode_workspace_bytes(-1, 16, 128) == 0
+    assert _raw_decode(batch=0, q=None, k=None, v=None, o=None, sl=None, ws=None) == bsa.BSA_OK
+
+
 def test_dense_ref_rejects_small_workspace():
     L = bsa.lib()
     need = bsa.bsa_dense_route_workspace_bytes(4096, 64)

@@ -189,3 +189,62 @@ def test_bf16_inputs_are_read_exactly():
     a = A.attention(q, k, v, 8, rp, ci)
     b = A.attention(q.double(), k.double(), v.double(), 8, rp, ci)
     assert np.array_equal(a, b)
+
+
+# --- selected-page decode ------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_decode_matches_masked_sdpa(kind):
+    # one query per sequence against the library routine with an explicit token mask whose
+    # membership is restated independently of oracle.routes
+    n_max, B, hq, hkv, d = 90, 8, 4, 2, 8
+    lens = [1, 8, 9, 57, 90]
+    g = torch.Generator("cpu").manual_seed(21)
+    q = torch.randn(len(lens), hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(len(lens), hkv, n_max, d, generator=g, dtype=torch.float64)
+    v = torch.randn(len(lens), hkv, n_max, d, generator=g, dtype=torch.float64)
+    rp, ci = R.route_csr(kind, n_max, B)
+    got, lse = A.decode_attention(q, k, v, lens, B, rp, ci, return_lse=True)
+    for bi, ln in enumerate(lens):
+        t = ln - 1
+        mask = torch.tensor([[s <= t and _member(kind, t // B, s // B) for s in range(n_max)]])
+        kk, vv = k[bi].repeat_interleave(2, 0), v[bi].repeat_interleave(2, 0)
+        ref = F.scaled_dot_product_attention(q[bi][:, None], kk, vv, attn_mask=mask)[:, 0].numpy()
+        assert np.abs(got[bi] - ref).max() < 1e-12
+        sel = [s for s in range(n_max) if mask[0, s]]
+        sc = (kk[:, sel] @ q[bi][:, :, None])[..., 0].numpy() / math.sqrt(d)  # [hq, |sel|]
+        want_lse = np.log(np.exp(sc).sum(-1))
+        assert np.abs(lse[bi] - want_lse).max() < 1e-12
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_decode_agrees_with_prefill_row(kind):
+    # decode-reference agreement: the decoded token t gives row t of the prefill output
+    n, B = 120, 16
+    q, k, v = _qkv(2, 4, 2, n, 8, seed=22)
+    rp, ci = R.route_csr(kind, n, B)
+    full = A.attention(q, k, v, B, rp, ci)
+    for t in (0, 15, 16, 77, 119):
+        got = A.decode_attention(q[:, :, t], k, v, [t + 1, t + 1], B, rp, ci)
+        assert np.abs(got - full[:, :, t]).max() < 1e-12
+
+
+def test_decode_closed_forms():
+    # K = 0: uniform weights over the selected keys; a one-token cache returns v[0]; lengths are
+    # clamped to [1, n_max]
+    n_max, B = 200, 16
+    s = torch.arange(n_max, dtype=torch.float64)
+    v = torch.stack([torch.ones(n_max), s, s * s], -1)[None, None]
+    k = torch.zeros(1, 1, n_max, 3, dtype=torch.float64)
+    q = torch.randn(1, 1, 3, dtype=torch.float64)
+    rp, ci = R.route_csr(R.BF1, n_max, B)
+    for ln in (1, 17, 133, 200):
+        t = ln - 1
+        sel = [x for x in range(t + 1) if _member(R.BF1, t // B, x // B)]
+        o, lse = A.decode_attention(q, k, v, [ln], B, rp, ci, return_lse=True)
+        assert abs(o[0, 0, 1] - np.mean(sel)) < 1e-9 and abs(lse[0, 0] - math.log(len(sel))) < 1e-12
+    o1 = A.decode_attention(q, torch.randn(1, 1, n_max, 3, dtype=torch.float64), v, [1], B, rp, ci)
+    assert np.array_equal(o1[0, 0], v[0, 0, 0].numpy())
+    assert np.array_equal(A.decode_attention(q, k, v, [0], B, rp, ci), A.decode_attention(q, k, v, [1], B, rp, ci))
+    assert np.array_equal(A.decode_attention(q, k, v, [999], B, rp, ci),
+                          A.decode_attention(q, k, v, [200], B, rp, ci))
