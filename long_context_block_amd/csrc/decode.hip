@@ -40,6 +40,41 @@ __device__ inline float elem(const uint4& raw, int e) {
 
 __device__ inline int64_t clamp_len(int64_t len, int64_t n_max) { return len < 1 ? 1 : (len > n_max ? n_max : len); }
 
+// Lane exchanges without LDS: DPP within a row of 16 lanes, v_permlane16/32_swap across rows.
+// XOR<m>(x) returns x of lane (lane ^ m) for m in {1, 2, 8, 16, 32}; HALF(x) returns x of the
+// lane mirrored within its group of 8 (lane ^ 7), which pairs each quad with the other quad of
+// the group.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int M>
+__device__ inline float xor_lane(float x) {
+    if constexpr (M == 1) return dpp<0xb1>(x);        // quad_perm [1, 0, 3, 2]
+    else if constexpr (M == 2) return dpp<0x4e>(x);   // quad_perm [2, 3, 0, 1]
+    else if constexpr (M == 8) return dpp<0x128>(x);  // row_ror:8
+    else {
+        const uint32_t u = __float_as_uint(x);
+        const auto sw = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        // even rows (halves) find the partner in the second result, odd ones in the first
+        const bool lo = M == 16 ? ((threadIdx.x >> 4) & 1) == 0 : (threadIdx.x & 32) == 0;
+        return __uint_as_float(lo ? sw[1] : sw[0]);
+    }
+}
+__device__ inline float half_mirror(float x) { return dpp<0x141>(x); }  // row_half_mirror
+
+// sum over the N consecutive lanes of an aligned group (N in {8, 16, 32}); every lane gets it
+template <int N>
+__device__ inline float group_sum(float x) {
+    x += xor_lane<1>(x);
+    x += xor_lane<2>(x);
+    x += half_mirror(x);  // the two quads of a group of 8 are uniform: pair them
+    if constexpr (N >= 16) x += xor_lane<8>(x);
+    if constexpr (N >= 32) x += xor_lane<16>(x);
+    return x;
+}
+
 template <typename T, int D, int GC>
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
@@ -47,30 +82,31 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     constexpr int RPI = 64 / LPR;        // key rows per load instruction
     constexpr int NI = kSub / RPI;       // load instructions per sub-block
     static_assert(LPR * VEC == D && RPI * LPR == 64 && NI * RPI == kSub, "lane layout");
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row groups");
     const int lane = threadIdx.x;
     const int r = lane / LPR;  // key row within a load instruction
     const int c = lane % LPR;  // 16-byte column chunk
 
-    int64_t u = blockIdx.x;
-    const int s = (int)(u % p.splits);
+    int u = blockIdx.x;
+    const int s = u % p.splits;
     u /= p.splits;
-    const int hc = (int)(u % p.hchunks);
+    const int hc = u % p.hchunks;
     u /= p.hchunks;
-    const int g = (int)(u % p.heads_kv);
+    const int g = u % p.heads_kv;
     const int64_t b = u / p.heads_kv;
     const int G = p.heads_q / p.heads_kv;
     const int h0 = g * G + hc * GC;
 
     const int64_t t = clamp_len(p.seq_lens[b], p.n_max) - 1;
-    const int64_t i = t / p.block;
-    int64_t e0 = p.row_ptr[i], e1 = p.row_ptr[i + 1];
-    e0 = e0 < 0 ? 0 : (e0 > p.nnz ? p.nnz : e0);
-    e1 = e1 < e0 ? e0 : (e1 > p.nnz ? p.nnz : e1);
-    const int spb = p.block / kSub;
-    const int64_t nsub = (e1 - e0) * spb;
+    const int i = (int)(t / p.block);
+    int e0 = p.row_ptr[i], e1 = p.row_ptr[i + 1];
+    e0 = e0 < 0 ? 0 : (e0 > p.nnz ? (int)p.nnz : e0);
+    e1 = e1 < e0 ? e0 : (e1 > p.nnz ? (int)p.nnz : e1);
+    const int sh = p.block == 128 ? 2 : 1;  // log2 of the 32-key sub-blocks per block
+    const int nsub = (e1 - e0) << sh;
 
-    const T* Kh = (const T*)p.k + (b * p.heads_kv + g) * p.n_max * D;
-    const T* Vh = (const T*)p.v + (b * p.heads_kv + g) * p.n_max * D;
+    const T* Kh = (const T*)p.k + (b * p.heads_kv + g) * p.n_max * D + c * VEC;
+    const T* Vh = (const T*)p.v + (b * p.heads_kv + g) * p.n_max * D + c * VEC;
 
     float q[GC][VEC], acc[GC][VEC], m[GC], l[GC];
 #pragma unroll
@@ -85,18 +121,44 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
         l[h] = 0.f;
     }
 
-    for (int64_t sb = s; sb < nsub; sb += p.splits) {
-        const int64_t j = p.col_idx[e0 + sb / spb];
-        if (j < 0 || j > i) continue;  // malformed (non-causal) entry: nothing selected
-        const int64_t k0 = j * p.block + (sb % spb) * kSub;
-        if (k0 > t) continue;  // the whole sub-block is in the future of token t
-        uint4 kf[NI], vf[NI];  // raw 16-byte vectors, converted on use
+    // first key of the next sub-block of this split at or after sb that holds a selected key
+    // (-1: none left); sub-blocks of malformed (non-causal) entries and those wholly past t are
+    // skipped
+    auto next_sub = [&](int& sb) -> int64_t {
+        for (; sb < nsub; sb += p.splits) {
+            const int j = p.col_idx[e0 + (sb >> sh)];
+            if (j < 0 || j > i) continue;
+            const int64_t k0 = (int64_t)j * p.block + ((sb & ((1 << sh) - 1)) << 5);
+            if (k0 <= t) return k0;
+        }
+        return -1;
+    };
+    uint4 kf[NI], vf[NI];  // raw 16-byte vectors of the current sub-block, converted on use
+    auto load = [&](int64_t k0) {
 #pragma unroll
         for (int x = 0; x < NI; ++x) {
             const int64_t key = k0 + x * RPI + r;
             const int64_t kr = key < t ? key : t;  // rows past t are masked; read row t instead
-            kf[x] = *(const uint4*)(Kh + kr * D + c * VEC);
-            vf[x] = *(const uint4*)(Vh + kr * D + c * VEC);
+            kf[x] = *(const uint4*)(Kh + kr * D);
+            vf[x] = *(const uint4*)(Vh + kr * D);
+        }
+    };
+    int sb = s;
+    int64_t k0 = next_sub(sb);
+    if (k0 >= 0) load(k0);
+    while (k0 >= 0) {
+        // the next sub-block's rows are requested before this one is consumed
+        int sbn = sb + p.splits;
+        const int64_t k1 = next_sub(sbn);
+        uint4 kn[NI], vn[NI];
+        if (k1 >= 0) {
+#pragma unroll
+            for (int x = 0; x < NI; ++x) {
+                const int64_t key = k1 + x * RPI + r;
+                const int64_t kr = key < t ? key : t;
+                kn[x] = *(const uint4*)(Kh + kr * D);
+                vn[x] = *(const uint4*)(Vh + kr * D);
+            }
         }
 #pragma unroll
         for (int h = 0; h < GC; ++h) {
@@ -107,13 +169,14 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
                 float part = 0.f;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) part = fmaf(q[h][e], elem<T>(kf[x], e), part);
-#pragma unroll
-                for (int o = 1; o < LPR; o <<= 1) part += __shfl_xor(part, o);
+                part = group_sum<LPR>(part);
                 sc[x] = (k0 + x * RPI + r <= t) ? part : -INFINITY;
                 mx = fmaxf(mx, sc[x]);
             }
-#pragma unroll
-            for (int o = LPR; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            // max over the row groups (scores are uniform within a group)
+            if constexpr (LPR <= 8) mx = fmaxf(mx, xor_lane<8>(mx));
+            if constexpr (LPR <= 16) mx = fmaxf(mx, xor_lane<16>(mx));
+            mx = fmaxf(mx, xor_lane<32>(mx));
             const float mnew = fmaxf(m[h], mx);  // finite: key k0 <= t is selected
             const float alpha = __builtin_amdgcn_exp2f(m[h] - mnew);
             float psum = 0.f;
@@ -129,17 +192,26 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
             l[h] = l[h] * alpha + psum;
             m[h] = mnew;
         }
+        k0 = k1;
+        sb = sbn;
+#pragma unroll
+        for (int x = 0; x < NI; ++x) {
+            kf[x] = kn[x];
+            vf[x] = vn[x];
+        }
     }
 
     // sum over the key rows held by the different row groups of the wavefront
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
+        auto across = [&](float x) {
+            if constexpr (LPR <= 8) x += xor_lane<8>(x);
+            if constexpr (LPR <= 16) x += xor_lane<16>(x);
+            return x + xor_lane<32>(x);
+        };
+        l[h] = across(l[h]);
 #pragma unroll
-        for (int o = LPR; o < 64; o <<= 1) {
-            l[h] += __shfl_xor(l[h], o);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
-        }
+        for (int e = 0; e < VEC; ++e) acc[h][e] = across(acc[h][e]);
         if (r == 0) {
             float* dst = p.ws + ((b * p.heads_q + h0 + h) * p.splits + s) * (D + 2);
 #pragma unroll
@@ -170,16 +242,33 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) L += __shfl_xor(L, o);
     const float inv = 1.0f / L;
+    // lane = column (D / 64 columns each); the partials are read 16 at a time so that their
+    // loads are in flight together
+    constexpr int NC = D / 64;
+    constexpr int U = 16;
+    float o[NC] = {};
+    for (int s0 = 0; s0 < S; s0 += U) {
+        float a[U][NC], ws[U];
 #pragma unroll
-    for (int cc = 0; cc < D / 64; ++cc) {
+        for (int x = 0; x < U; ++x) {
+            const int s = s0 + x < S ? s0 + x : S - 1;
+            ws[x] = s0 + x < S ? __shfl(w, s) : 0.f;
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) a[x][cc] = base[s * (D + 2) + cc * 64 + lane];
+        }
+#pragma unroll
+        for (int x = 0; x < U; ++x)
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) o[cc] = fmaf(ws[x], a[x][cc], o[cc]);
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
         const int col = cc * 64 + lane;
-        float o = 0.f;
-        for (int s = 0; s < S; ++s) o = fmaf(__shfl(w, s), base[s * (D + 2) + col], o);
-        o *= inv;
+        const float v = o[cc] * inv;
         if constexpr (sizeof(T) == 2)
-            ((__bf16*)p.o)[bh * D + col] = (__bf16)o;  // round to nearest even
+            ((__bf16*)p.o)[bh * D + col] = (__bf16)v;  // round to nearest even
         else
-            ((float*)p.o)[bh * D + col] = o;
+            ((float*)p.o)[bh * D + col] = v;
     }
     if (p.lse && lane == 0) p.lse[bh] = (M + __log2f(L)) * 0.69314718055994530942f;
 }
