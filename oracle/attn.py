@@ -144,3 +144,65 @@ def decode_attention(q, k_cache, v_cache, seq_lens, B: int, row_ptr, col_idx, sc
             out[bi, h] = (E / den) @ V[bi, h // G]
             lse[bi, h] = mx + np.log(den)
     return (out, lse) if return_lse else out
+
+
+def attention_backward(q, k, v, d_o, B: int, row_ptr, col_idx, scale: float | None = None,
+                       q_rows=None, k_rows=None):
+    """Gradients of block-sparse attention, fp64 (the "gradients" correctness gate of "BF1 ...",
+    section 4).
+
+    With O = P V, P = softmax(S) row-wise over the selected keys, S = scale Q K^T, and
+    f = sum(O * dO) for the given upstream gradient dO, the chain rule gives, per (b, head):
+
+        dV = P^T dO                       (summed over the query heads sharing a key/value head)
+        dP = dO V^T
+        dS = P * (dP - D),  D[t] = sum_d dO[t, d] O[t, d]   (= sum_s P[t, s] dP[t, s])
+        dQ = scale * dS K
+        dK = scale * dS^T Q               (summed over the query heads sharing a key/value head)
+
+    Excluded pairs have P = 0 and therefore dS = 0: no gradient flows through them.  O is
+    recomputed here from the inputs.  ``q_rows`` / ``k_rows`` restrict the returned dq rows and
+    dk/dv rows (default: all); only the query blocks those rows need are evaluated (dq[t] needs
+    its own block; dk[s], dv[s] need every query block whose route row holds block(s)).
+    Returns (dq [b, Hq, len(q_rows), d], dk [b, Hkv, len(k_rows), d], dv [same]) in float64.
+    """
+    Q, K, V, dO = _to_f64(q), _to_f64(k), _to_f64(v), _to_f64(d_o)
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    G = hq // hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / np.sqrt(d)
+    q_rows = np.arange(n) if q_rows is None else np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.arange(n) if k_rows is None else np.asarray(k_rows, dtype=np.int64)
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    nqb = len(rp) - 1
+    kblocks = set(int(x) for x in np.unique(k_rows // B))
+    need = set(int(x) for x in np.unique(q_rows // B))
+    for i in range(nqb):
+        if kblocks & set(int(j) for j in ci[rp[i]:rp[i + 1]]):
+            need.add(i)
+    dq = np.zeros((b, hq, len(q_rows), d))
+    dk = np.zeros((b, hkv, n, d))
+    dv = np.zeros((b, hkv, n, d))
+    qpos = {int(t): x for x, t in enumerate(q_rows)}
+    for i in sorted(need):
+        r = np.arange(i * B, min((i + 1) * B, n))
+        M = token_mask(n, B, row_ptr, col_idx, r)
+        for bi in range(b):
+            for h in range(hq):
+                kv = h // G
+                S = np.where(M, (Q[bi, h, r] @ K[bi, kv].T) * scale, -np.inf)
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                P = E / E.sum(axis=1, keepdims=True)
+                O = P @ V[bi, kv]
+                dP = dO[bi, h, r] @ V[bi, kv].T
+                Dt = (dO[bi, h, r] * O).sum(axis=1, keepdims=True)
+                dS = P * (dP - Dt)
+                dQ = scale * (dS @ K[bi, kv])
+                for x, t in enumerate(r):
+                    if int(t) in qpos:
+                        dq[bi, h, qpos[int(t)]] = dQ[x]
+                dk[bi, kv] += scale * (dS.T @ Q[bi, h, r])
+                dv[bi, kv] += P.T @ dO[bi, h, r]
+    return dq, dk[:, :, k_rows], dv[:, :, k_rows]

@@ -248,3 +248,86 @@ def test_decode_closed_forms():
     assert np.array_equal(A.decode_attention(q, k, v, [0], B, rp, ci), A.decode_attention(q, k, v, [1], B, rp, ci))
     assert np.array_equal(A.decode_attention(q, k, v, [999], B, rp, ci),
                           A.decode_attention(q, k, v, [200], B, rp, ci))
+
+
+# --- backward ------------------------------------------------------------------------------
+
+def _autograd_ref(q, k, v, d_o, kind, B, nl=2):
+    """torch autograd through the library attention with an independently restated mask."""
+    n = q.shape[2]
+    G = q.shape[1] // k.shape[1]
+    mask = torch.tensor([[s <= t and _member(kind, t // B, s // B, nl) for s in range(n)] for t in range(n)])
+    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qq, kk.repeat_interleave(G, 1), vv.repeat_interleave(G, 1), attn_mask=mask)
+    o.backward(d_o)
+    return qq.grad.numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n,B", [(96, 16), (75, 8)])
+def test_backward_matches_autograd(kind, n, B):
+    q, k, v = _qkv(2, 4, 2, n, 8, seed=41)
+    d_o = torch.randn(q.shape, generator=torch.Generator("cpu").manual_seed(42), dtype=torch.float64)
+    rp, ci = R.route_csr(kind, n, B)
+    dq, dk, dv = A.attention_backward(q, k, v, d_o, B, rp, ci)
+    rq, rk, rv = _autograd_ref(q, k, v, d_o, kind, B)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.abs(got - ref).max() < 1e-10
+
+
+def test_backward_finite_differences():
+    # central differences of f = sum(O * dO) on a tiny BF1 problem, every input element
+    n, B, d = 20, 4, 3
+    q, k, v = _qkv(1, 2, 1, n, d, seed=43)
+    d_o = torch.randn(q.shape, generator=torch.Generator("cpu").manual_seed(44), dtype=torch.float64)
+    rp, ci = R.route_csr(R.BF1, n, B)
+    dq, dk, dv = A.attention_backward(q, k, v, d_o, B, rp, ci)
+
+    def f(qq, kk, vv):
+        return float((A.attention(qq, kk, vv, B, rp, ci) * d_o.numpy()).sum())
+
+    h = 1e-6
+    for t, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(*t.shape):
+            tp, tm = t.clone(), t.clone()
+            tp[idx] += h
+            tm[idx] -= h
+            args_p = [tp if x is t else x for x in (q, k, v)]
+            args_m = [tm if x is t else x for x in (q, k, v)]
+            fd = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-6 * max(1.0, abs(g[idx])), (idx, fd, g[idx])
+
+
+def test_backward_gqa_sums_repeated_heads():
+    q, k, v = _qkv(1, 6, 2, 64, 8, seed=45)
+    d_o = torch.randn(q.shape, generator=torch.Generator("cpu").manual_seed(46), dtype=torch.float64)
+    rp, ci = R.route_csr(R.STATIC_RANDOM, 64, 8)
+    dq, dk, dv = A.attention_backward(q, k, v, d_o, 8, rp, ci)
+    rq, rk, rv = A.attention_backward(q, k.repeat_interleave(3, 1), v.repeat_interleave(3, 1), d_o, 8, rp, ci)
+    assert np.abs(dq - rq).max() < 1e-12
+    assert np.abs(dk - rk.reshape(1, 2, 3, 64, 8).sum(2)).max() < 1e-12
+    assert np.abs(dv - rv.reshape(1, 2, 3, 64, 8).sum(2)).max() < 1e-12
+
+
+def test_backward_row_subsets_match_full():
+    n, B = 200, 16
+    q, k, v = _qkv(1, 2, 2, n, 8, seed=47)
+    d_o = torch.randn(q.shape, generator=torch.Generator("cpu").manual_seed(48), dtype=torch.float64)
+    rp, ci = R.route_csr(R.BF1, n, B)
+    full = A.attention_backward(q, k, v, d_o, B, rp, ci)
+    qr, kr = np.array([0, 17, 100, 199]), np.array([3, 64, 150, 199])
+    sub = A.attention_backward(q, k, v, d_o, B, rp, ci, q_rows=qr, k_rows=kr)
+    assert np.array_equal(sub[0], full[0][:, :, qr])
+    assert np.abs(sub[1] - full[1][:, :, kr]).max() < 1e-12 and np.abs(sub[2] - full[2][:, :, kr]).max() < 1e-12
+
+
+def test_backward_excluded_keys_get_no_gradient():
+    # block-diagonal route: a key's gradient comes only from its own chunk's queries, so keys of
+    # a chunk whose dO is zero get exactly zero dk, dv
+    n, B = 64, 16
+    q, k, v = _qkv(1, 1, 1, n, 4, seed=49)
+    d_o = torch.randn(q.shape, generator=torch.Generator("cpu").manual_seed(50), dtype=torch.float64)
+    d_o[:, :, 16:32] = 0
+    rp, ci = R.route_csr(R.BLOCK_DIAGONAL, n, B)
+    dq, dk, dv = A.attention_backward(q, k, v, d_o, B, rp, ci)
+    assert (dk[:, :, 16:32] == 0).all() and (dv[:, :, 16:32] == 0).all() and (dq[:, :, 16:32] == 0).all()
