@@ -108,6 +108,17 @@ bsa_status bsa_build_route(const bsa_route_spec* spec, int64_t n, int32_t block,
                            int64_t* nnz_out, hipStream_t stream);
 
 /*
+ * bsa_build_route_transpose — the transposed route: row j lists, ascending, the query blocks i
+ * whose row of (row_ptr, col_idx) holds key block j (the readers of block j; for a valid route
+ * the first entry is j itself).  The gradients of K and V walk these rows (bsa_backward).
+ * Input: a route accepted by bsa_check_route, nqb + 1 row pointers, nnz entries (device).
+ * Output (device, caller-owned): t_row_ptr int32[nqb+1], t_col_idx int32[nnz] (a valid route
+ * transposes to exactly nnz entries).  Integer kernels on `stream`; memory-safe on any input.
+ */
+bsa_status bsa_build_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
+                                     int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream);
+
+/*
  * bsa_forward — block-sparse attention forward over a CSR route (see the top of this file).
  *
  * Layout (device, caller-owned, contiguous, d innermost, 16-byte aligned base pointers):
@@ -150,6 +161,36 @@ bsa_status bsa_dense_causal_ref(const void* q, const void* k, const void* v, voi
 
 /* Workspace bytes bsa_dense_causal_ref needs for n tokens at width block (0 on bad input). */
 size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block);
+
+/*
+ * bsa_backward — gradients of bsa_forward (the "gradients" correctness gate of "BF1 ...",
+ * section 4).  With P the forward's weights (recomputed from q, k and its log-sum-exp) and
+ * D[t] = sum_d d_o[t, d] o[t, d]:
+ *
+ *     dv = P^T d_o,   dS = P * (d_o v^T - D),   dq = scale * dS k,   dk = scale * dS^T q
+ *
+ * per head, dk and dv summed over the query heads sharing a key/value head (h / G).  Excluded
+ * pairs carry no gradient.
+ * Inputs (device, caller-owned, contiguous, 16-byte aligned): q, k, v, o, d_o as for
+ * bsa_forward (o its output, d_o the upstream gradient of o, same shape); lse float32
+ * [batch, heads_q, n] from bsa_forward (required); the route (row_ptr, col_idx, nnz) and its
+ * transpose from bsa_build_route_transpose (t_row_ptr, t_col_idx).  Outputs: dq like q, dk and
+ * dv like k and v, in `dtype`.  workspace: float32 scratch of at least
+ * bsa_backward_workspace_bytes(...) bytes (D, the segment table of the transposed rows, and fp32
+ * partial dk/dv of key blocks whose readers are split over several work-groups); its contents
+ * on entry do not matter.  Supported: dtype BF16; d in {64, 128}; block in {64, 128}; any n >= 0.
+ * Five kernels on `stream`; the result is deterministic (no atomics).
+ */
+bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                        const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,
+                        int32_t heads_kv, int64_t n, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                        const int32_t* row_ptr, const int32_t* col_idx, int64_t nnz,
+                        const int32_t* t_row_ptr, const int32_t* t_col_idx,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes bsa_backward needs (0 on bad input). */
+size_t bsa_backward_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                                    int32_t block, int64_t nnz);
 
 /*
  * bsa_decode — selected-page decode: one new query token per sequence against the key/value

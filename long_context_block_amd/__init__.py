@@ -33,7 +33,8 @@ BSA_ROUTE_STATIC_RANDOM = 3
 BSA_ROUTE_SLIDING_WINDOW = 4
 
 EXPORTS = ("bsa_build_route", "bsa_forward", "bsa_dense_causal_ref", "bsa_dense_route_workspace_bytes",
-           "bsa_decode", "bsa_decode_workspace_bytes", "bsa_check_route", "bsa_status_string", "bsa_last_error")
+           "bsa_decode", "bsa_decode_workspace_bytes", "bsa_build_route_transpose", "bsa_backward",
+           "bsa_backward_workspace_bytes", "bsa_check_route", "bsa_status_string", "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -77,6 +78,13 @@ def lib() -> ctypes.CDLL:
         L.bsa_decode.restype = ctypes.c_int
         L.bsa_decode_workspace_bytes.argtypes = [i32, i32, i32]
         L.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_build_route_transpose.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.bsa_build_route_transpose.restype = ctypes.c_int
+        L.bsa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, ctypes.c_int,
+                                   f32, vp, vp, i64, vp, vp, vp, ctypes.c_size_t, vp]
+        L.bsa_backward.restype = ctypes.c_int
+        L.bsa_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i64]
+        L.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_check_route.argtypes = [vp, vp, i64, i64]
         L.bsa_check_route.restype = ctypes.c_int
         L.bsa_status_string.argtypes = [ctypes.c_int]
@@ -226,6 +234,67 @@ def bsa_decode(q, k_cache, v_cache, o, seq_lens, row_ptr, col_idx, block: int, w
     wp = _dev_ptr(workspace, "workspace", torch.float32)
     _check(lib().bsa_decode(*ptrs, lp, sp, b, hq, hkv, n_max, d, block, dt, float(scale), rp, ci, col_idx.numel(),
                             wp, workspace.numel() * 4, _stream(stream)))
+
+
+def bsa_build_route_transpose(row_ptr, col_idx, t_row_ptr, t_col_idx, stream=None) -> None:
+    """Write the transposed route (readers of every key block) into t_row_ptr/t_col_idx (int32 GPU)."""
+    import torch
+    nqb = row_ptr.numel() - 1
+    nnz = col_idx.numel()
+    if t_row_ptr.numel() != nqb + 1 or t_col_idx.numel() != nnz:
+        raise ValueError("t_row_ptr must have nqb + 1 entries and t_col_idx nnz entries")
+    ptrs = [_dev_ptr(x, nm, torch.int32, allow_none=(x is None or x.numel() == 0))
+            for x, nm in ((row_ptr, "row_ptr"), (col_idx, "col_idx"), (t_row_ptr, "t_row_ptr"), (t_col_idx, "t_col_idx"))]
+    _check(lib().bsa_build_route_transpose(ptrs[0], ptrs[1], nqb, nnz, ptrs[2], ptrs[3], _stream(stream)))
+
+
+def bsa_backward_workspace_bytes(batch: int, heads_q: int, heads_kv: int, n: int, d: int, block: int, nnz: int) -> int:
+    return int(lib().bsa_backward_workspace_bytes(batch, heads_q, heads_kv, n, d, block, nnz))
+
+
+def bsa_backward(q, k, v, o, d_o, lse, dq, dk, dv, row_ptr, col_idx, t_row_ptr, t_col_idx, block: int, workspace,
+                 scale: float = 0.0, stream=None) -> None:
+    """dq, dk, dv = gradients of bsa_forward for upstream gradient d_o (see include/bsa.h)."""
+    import torch
+    dt = _dtype_code(q)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    for x, nm, shp in ((k, "k", (b, hkv, n, d)), (v, "v", (b, hkv, n, d)), (o, "o", (b, hq, n, d)),
+                       (d_o, "d_o", (b, hq, n, d)), (dq, "dq", (b, hq, n, d)), (dk, "dk", (b, hkv, n, d)),
+                       (dv, "dv", (b, hkv, n, d)), (lse, "lse", (b, hq, n))):
+        if tuple(x.shape) != shp:
+            raise ValueError(f"{nm} must have shape {shp}")
+    ptrs = [_dev_ptr(x, nm, q.dtype) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o"))]
+    lp = _dev_ptr(lse, "lse", torch.float32)
+    gp = [_dev_ptr(x, nm, q.dtype) for x, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    rp = _dev_ptr(row_ptr, "row_ptr", torch.int32)
+    ci = _dev_ptr(col_idx, "col_idx", torch.int32)
+    trp = _dev_ptr(t_row_ptr, "t_row_ptr", torch.int32)
+    tci = _dev_ptr(t_col_idx, "t_col_idx", torch.int32)
+    wp = _dev_ptr(workspace, "workspace")
+    _check(lib().bsa_backward(*ptrs, lp, *gp, b, hq, hkv, n, d, block, dt, float(scale), rp, ci, col_idx.numel(),
+                              trp, tci, wp, workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def build_route_transpose(row_ptr, col_idx, stream=None):
+    """Allocate and build the transposed route on the GPU; returns (t_row_ptr, t_col_idx)."""
+    import torch
+    t_row_ptr = torch.empty_like(row_ptr)
+    t_col_idx = torch.empty(max(col_idx.numel(), 1), dtype=torch.int32, device=col_idx.device)[:col_idx.numel()]
+    bsa_build_route_transpose(row_ptr, col_idx, t_row_ptr, t_col_idx, stream)
+    return t_row_ptr, t_col_idx
+
+
+def backward(q, k, v, o, d_o, lse, row_ptr, col_idx, block: int, t_route=None, scale: float = 0.0, stream=None):
+    """Allocate the gradients and workspace (and the transposed route unless given) and run bsa_backward."""
+    import torch
+    b, hq, n, d = q.shape
+    t_row_ptr, t_col_idx = t_route if t_route is not None else build_route_transpose(row_ptr, col_idx, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = bsa_backward_workspace_bytes(b, hq, k.shape[1], n, d, block, col_idx.numel())
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    bsa_backward(q, k, v, o, d_o, lse, dq, dk, dv, row_ptr, col_idx, t_row_ptr, t_col_idx, block, ws, scale, stream)
+    return dq, dk, dv
 
 
 def bsa_check_route(row_ptr, col_idx) -> None:

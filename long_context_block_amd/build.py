@@ -34,6 +34,7 @@ HIPCC_FLAGS = [
 EXTRA_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
     "fwd_bf16_basic.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "bwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -62,10 +63,10 @@ def _compile(hipcc: str, src: str, verbose: bool) -> str:
 
 
 def check_m0(hipcc: str, src: str) -> None:
-    """The asynchronous LDS copy helper sets M0 in inline asm; M0 is reserved by the compiler and
+    """The asynchronous LDS copy helpers set M0 in inline asm; M0 is reserved by the compiler and
     cannot be declared clobbered, so the generated code must contain no other M0 user.  Compile
-    the device code to assembly and check that every M0 write is the helper's, immediately
-    followed by its global_load_lds_dwordx4, and that nothing else references M0."""
+    the device code to assembly and check that every M0 write is a helper's, immediately
+    followed by its global_load_lds_dword(x4), and that nothing else references M0."""
     out = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".s")
     cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "--cuda-device-only", "-S", src,
            "-o", out]
@@ -77,7 +78,7 @@ def check_m0(hipcc: str, src: str) -> None:
         if ln.startswith(";") or "m0" not in ln.replace(",", " ").split():
             continue
         nxt = lines[k + 1] if k + 1 < len(lines) else ""
-        if not (ln.startswith("s_mov_b32 m0,") and nxt.startswith("global_load_lds_dwordx4")):
+        if not (ln.startswith("s_mov_b32 m0,") and nxt.startswith("global_load_lds_dword")):
             raise RuntimeError(f"{src}: unexpected M0 use in generated code: {ln!r}")
 
 

@@ -205,6 +205,74 @@ bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, flo
                        nnz, stream);
 }
 
+bsa_status bsa_build_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
+                                     int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream) {
+    if (nqb < 0 || nnz < 0 || nnz > INT32_MAX || nqb > INT32_MAX - 1)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "need 0 <= nqb < 2^31 - 1 and 0 <= nnz < 2^31");
+    if (!row_ptr || !t_row_ptr) return fail(BSA_ERR_INVALID_ARGUMENT, "row_ptr and t_row_ptr must be non-NULL");
+    if (nnz > 0 && (!col_idx || !t_col_idx))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "col_idx and t_col_idx must be non-NULL when nnz > 0");
+    const hipError_t e = bsa::launch_route_transpose(row_ptr, col_idx, nqb, nnz, t_row_ptr, t_col_idx, stream);
+    if (e != hipSuccess) return device_error(e, "route transpose launch");
+    return ok();
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}
+
+size_t bsa_backward_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                                    int32_t block, int64_t nnz) {
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || n < 0 || d < 1 || block < 64 || nnz < 0)
+        return 0;
+    const int64_t nqb = (n + block - 1) / block;
+    const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
+    return align256((size_t)batch * heads_q * n * sizeof(float)) + align256((size_t)(nqb + 1) * sizeof(int32_t)) +
+           (size_t)batch * heads_kv * segs * 2 * block * d * sizeof(float);
+}
+
+bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o, const float* lse,
+                        void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n,
+                        int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
+                        const int32_t* col_idx, int64_t nnz, const int32_t* t_row_ptr, const int32_t* t_col_idx,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    bsa_status s = validate_forward(q, k, v, dq, nullptr, batch, heads_q, heads_kv, n, d, block, dtype, row_ptr,
+                                    col_idx, nnz, true);
+    if (s != BSA_OK) return s;
+    if (dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "the backward supports bf16 only");
+    if (!(scale <= 0.f) && !std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (batch == 0 || n == 0) return ok();
+    if (!o || !d_o || !lse || !dk || !dv || !t_row_ptr || !t_col_idx || !workspace)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "o, d_o, lse, dk, dv, the transposed route and workspace must be non-NULL");
+    if (!aligned16(o) || !aligned16(d_o) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "o, d_o, dk, dv and workspace must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    const size_t need = bsa_backward_workspace_bytes(batch, heads_q, heads_kv, n, d, block, nnz);
+    if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
+    const int64_t nqb = (n + block - 1) / block;
+    const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
+    if ((int64_t)batch * heads_kv * segs > INT32_MAX || (int64_t)batch * heads_q * nqb > INT32_MAX)
+        return fail(BSA_ERR_UNSUPPORTED, "grid too large");
+    bsa::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.d_o = d_o; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.row_ptr = row_ptr; p.col_idx = col_idx; p.t_row_ptr = t_row_ptr; p.t_col_idx = t_col_idx;
+    char* ws = (char*)workspace;
+    p.dvec = (float*)ws;
+    ws += align256((size_t)batch * heads_q * n * sizeof(float));
+    p.seg_ptr = (int32_t*)ws;
+    ws += align256((size_t)(nqb + 1) * sizeof(int32_t));
+    p.part = (float*)ws;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv;
+    p.nqb = (int32_t)nqb; p.n = n; p.nnz = nnz; p.nseg_ub = segs;
+    const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
+    p.scale = (float)sc;
+    p.scale_log2 = (float)(sc * 1.4426950408889634073599);
+    const hipError_t e = bsa::launch_bwd_bf16(p, d, block, stream);
+    if (e != hipSuccess) return device_error(e, "backward launch");
+    return ok();
+}
+
 size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d) {
     if (batch < 0 || heads_q < 1 || d < 1) return 0;
     return (size_t)batch * heads_q * bsa::kDecodeMaxSplits * (d + 2) * sizeof(float);

@@ -46,6 +46,8 @@ __host__ __device__ inline int64_t route_row_count(int kind, int64_t i, int n_lo
 // the hipError_t of the launch.
 hipError_t launch_route_build(const bsa_route_spec& spec, int64_t nqb, int32_t* row_ptr,
                               int32_t* col_idx, hipStream_t stream);
+hipError_t launch_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
+                                  int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream);
 
 struct FwdParams {
     const void* q;
@@ -81,6 +83,35 @@ struct DecodeParams {
     float scale_log2;
 };
 constexpr int kDecodeMaxSplits = 64;
+
+struct BwdParams {
+    const void* q;    // [batch, heads_q, n, d]
+    const void* k;    // [batch, heads_kv, n, d]
+    const void* v;
+    const void* o;    // forward output
+    const void* d_o;  // upstream gradient of o
+    const float* lse; // forward log-sum-exp (natural log) [batch, heads_q, n]
+    void* dq;
+    void* dk;
+    void* dv;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    const int32_t* t_row_ptr;  // transposed route: query blocks reading key block j
+    const int32_t* t_col_idx;
+    float* dvec;      // workspace: D = rowsum(dO * O) [batch, heads_q, n]
+    int32_t* seg_ptr; // workspace: [nqb + 1] segment prefix of the transposed rows
+    float* part;      // workspace: [batch * heads_kv * nseg_ub, 2, block, d] partial dK, dV
+    int32_t batch, heads_q, heads_kv;
+    int32_t nqb;
+    int64_t n;
+    int64_t nnz;
+    int64_t nseg_ub;  // segments per (batch, kv head), upper bound
+    float scale;
+    float scale_log2;
+};
+
+int64_t bwd_segments_upper_bound(int64_t nqb, int64_t nnz, int heads_q, int heads_kv, int block);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, int block, hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t stream);

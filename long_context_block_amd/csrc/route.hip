@@ -160,7 +160,99 @@ __global__ __launch_bounds__(64) void route_fill_kernel(bsa_route_spec spec, int
     if (lane == 0) out[w] = (int32_t)i;
 }
 
+// ---- transposed route: for key block j, the query blocks i whose row holds j ------------------
+// Rows are read as ascending lists (bsa_check_route); membership of j in row i is a binary search.
+// Both passes visit i in ascending order, so the output rows are ascending and deterministic.
+
+__device__ inline bool row_holds(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+                                 int64_t nnz, int64_t i, int32_t j) {
+    int64_t lo = row_ptr[i], hi = row_ptr[i + 1];
+    lo = lo < 0 ? 0 : (lo > nnz ? nnz : lo);
+    hi = hi < lo ? lo : (hi > nnz ? nnz : hi);
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        const int32_t v = col_idx[mid];
+        if (v == j) return true;
+        if (v < j) lo = mid + 1; else hi = mid;
+    }
+    return false;
+}
+
+// one wavefront per key block j: t_row_ptr[j + 1] = #{i >= j : j in R(i)}
+__global__ __launch_bounds__(64) void route_t_count_kernel(const int32_t* __restrict__ row_ptr,
+                                                           const int32_t* __restrict__ col_idx, int64_t nqb,
+                                                           int64_t nnz, int32_t* __restrict__ t_row_ptr) {
+    const int64_t j = blockIdx.x;
+    const int lane = threadIdx.x;
+    int cnt = 0;
+    for (int64_t i = j + lane; i < nqb; i += 64) cnt += row_holds(row_ptr, col_idx, nnz, i, (int32_t)j) ? 1 : 0;
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) t_row_ptr[j + 1] = cnt;
+}
+
+// one work-group: in-place inclusive scan of t_row_ptr[1..nqb]; t_row_ptr[0] = 0
+__global__ __launch_bounds__(kScanThreads) void route_t_scan_kernel(int64_t nqb, int32_t* __restrict__ t_row_ptr) {
+    __shared__ int64_t part[kScanThreads];
+    const int t = threadIdx.x;
+    const int64_t per = (nqb + kScanThreads - 1) / kScanThreads;
+    const int64_t r0 = t * per;
+    const int64_t r1 = (r0 + per < nqb) ? r0 + per : nqb;
+    int64_t local = 0;
+    for (int64_t x = r0; x < r1; ++x) local += t_row_ptr[x + 1];
+    part[t] = local;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        const int64_t add = (t >= off) ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += add;
+        __syncthreads();
+    }
+    int64_t run = part[t] - local;
+    for (int64_t x = r0; x < r1; ++x) {
+        run += t_row_ptr[x + 1];
+        t_row_ptr[x + 1] = (int32_t)run;
+    }
+    if (t == 0) t_row_ptr[0] = 0;
+}
+
+// one wavefront per key block j: the query blocks i >= j whose row holds j, ascending
+__global__ __launch_bounds__(64) void route_t_fill_kernel(const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ col_idx, int64_t nqb,
+                                                          int64_t nnz, const int32_t* __restrict__ t_row_ptr,
+                                                          int32_t* __restrict__ t_col_idx) {
+    const int64_t j = blockIdx.x;
+    const int lane = threadIdx.x;
+    int64_t w = t_row_ptr[j];
+    const int64_t end = t_row_ptr[j + 1];
+    for (int64_t base = j; base < nqb; base += 64) {
+        const int64_t i = base + lane;
+        const bool sel = i < nqb && row_holds(row_ptr, col_idx, nnz, i, (int32_t)j);
+        const uint64_t mask = __ballot(sel);
+        const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+        if (sel && w + pos < end) t_col_idx[w + pos] = (int32_t)i;
+        w += __popcll(mask);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
+                                  int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream) {
+    if (nqb == 0) {
+        hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, t_row_ptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(route_t_count_kernel, dim3((unsigned)nqb), dim3(64), 0, stream, row_ptr, col_idx, nqb, nnz,
+                       t_row_ptr);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, t_row_ptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(route_t_fill_kernel, dim3((unsigned)nqb), dim3(64), 0, stream, row_ptr, col_idx, nqb, nnz,
+                       t_row_ptr, t_col_idx);
+    return hipGetLastError();
+}
 
 hipError_t launch_route_build(const bsa_route_spec& spec, int64_t nqb, int32_t* row_ptr,
                               int32_t* col_idx, hipStream_t stream) {

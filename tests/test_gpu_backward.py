@@ -1,0 +1,137 @@
+"""GPU backward (bsa_backward and bsa_build_route_transpose through the C ABI) against the fp64
+oracle.
+
+Transposed routes must be identical arrays.  Gradient bars (bf16 inputs and outputs): relative L2
+<= 1e-2 and max-abs <= 1e-2 * max|reference| per tensor.  Derivation: the kernels round three
+quantities to bf16 on the way (the weights P or the scores' gradient dS before each product, and
+the output), each with relative error <= 2^-9 ~ 1.95e-3, so a gradient formed as a sum of many such
+terms keeps a relative L2 error below about 3 x 1.95e-3 ~ 5.9e-3; 1e-2 leaves margin for the
+cancellation in dP - D.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_block_amd as bsa
+from oracle import attn as A
+from oracle import routes as R
+import synth
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.STATIC_RANDOM, R.SLIDING_WINDOW]
+RELL2, MAXREL = 1e-2, 1e-2
+
+
+def transpose_sets(rp, ci):
+    sets = R.csr_to_sets(rp, ci)
+    out = [[] for _ in sets]
+    for i, r in enumerate(sets):
+        for j in r:
+            out[j].append(i)
+    return out
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n,B", [(1, 64), (1000, 64), (4097, 128), (32768, 128)])
+def test_route_transpose_bit_exact(kind, n, B):
+    if kind == R.DENSE_CAUSAL and n > 5000:
+        pytest.skip("dense route at 256 blocks is covered at the smaller sizes")
+    rp, ci = bsa.build_route(bsa.route_spec(kind), n, B)
+    trp, tci = bsa.build_route_transpose(rp, ci)
+    torch.cuda.synchronize()
+    want_rp, want_ci = R.to_csr(transpose_sets(rp.cpu().numpy(), ci.cpu().numpy()))
+    assert np.array_equal(trp.cpu().numpy(), want_rp) and np.array_equal(tci.cpu().numpy(), want_ci)
+
+
+def grad_errors(got, ref):
+    got = got.double().cpu().numpy() if hasattr(got, "cpu") else got
+    d = got - ref
+    return float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300)), float(np.abs(d).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def run_backward(w, kind=None, seed=61, q_rows=None, k_rows=None):
+    kind = w.route_kind if kind is None else kind
+    q, k, v = synth.make_qkv(w)
+    g = torch.Generator("cpu").manual_seed(seed)
+    d_o = torch.randn(q.shape, generator=g).to(q.dtype)
+    rp, ci = bsa.build_route(bsa.route_spec(kind, w.n_local, w.keep_first, w.n_random, w.route_seed), w.n, w.block)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), d_o.cuda()
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, with_lse=True)
+    dq, dk, dv = bsa.backward(qd, kd, vd, o, dod, lse, rp, ci, w.block)
+    torch.cuda.synchronize()
+    rq, rk, rv = A.attention_backward(q, k, v, d_o, w.block, rp.cpu().numpy(), ci.cpu().numpy(),
+                                      q_rows=q_rows, k_rows=k_rows)
+    if q_rows is not None:
+        dq = dq[:, :, q_rows]
+    if k_rows is not None:
+        dk, dv = dk[:, :, k_rows], dv[:, :, k_rows]
+    return (dq, rq), (dk, rk), (dv, rv)
+
+
+REDUCED = [
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-d128-b128", n=1000),
+    synth.WORKLOADS["bf1_4k"].resized(name="mha-d128-b64", n=777, heads_q=2, heads_kv=2),
+    synth.WORKLOADS["bsbr_chunk_8k"].resized(name="mha-d64-b128", n=700, batch=2, heads_q=2, heads_kv=2),
+    synth.WORKLOADS["bf1_4k"].resized(name="gqa4-d64-b64", n=600, d=64, heads_q=4, heads_kv=1),
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-ragged", n=1, heads_q=2, heads_kv=1),
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-ragged-129", n=129, heads_q=2, heads_kv=1),
+]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("w", REDUCED, ids=[w.name for w in REDUCED])
+def test_backward_parity(w, kind):
+    print(f"backward {w.name} kind={kind}", flush=True)
+    for name, (got, ref) in zip(("dq", "dk", "dv"), run_backward(w, kind)):
+        rl2, mx = grad_errors(got, ref)
+        print(f"  {name}: rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)
+        assert rl2 <= RELL2 and mx <= MAXREL, (name, rl2, mx)
+
+
+def test_backward_long_reader_list_is_split():
+    # block 0 of a BF1 route is read by every query block: at 96 blocks its readers span several
+    # segments of the dK/dV pass, which are summed in order afterwards
+    w = synth.WORKLOADS["qwen3_32k"].resized(name="bf1-12k", n=12288)
+    rows = np.array([0, 1, 63, 127, 128, 4000, 12287])
+    for name, (got, ref) in zip(("dq", "dk", "dv"), run_backward(w, q_rows=rows, k_rows=rows)):
+        rl2, mx = grad_errors(got, ref)
+        print(f"  {name}: rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)
+        assert rl2 <= RELL2 and mx <= MAXREL, (name, rl2, mx)
+
+
+def test_backward_deterministic_and_no_future_gradient():
+    w = synth.WORKLOADS["qwen3_32k"].resized(n=900)
+    q, k, v = (x.cuda() for x in synth.make_qkv(w))
+    d_o = torch.randn(q.shape, device="cuda").to(q.dtype)
+    rp, ci = bsa.build_route(bsa.route_spec(w.route_kind), w.n, w.block)
+    o, lse = bsa.forward(q, k, v, rp, ci, w.block, with_lse=True)
+    g1 = bsa.backward(q, k, v, o, d_o, lse, rp, ci, w.block)
+    g2 = bsa.backward(q, k, v, o, d_o, lse, rp, ci, w.block)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    # an upstream gradient on the last 100 rows only: keys before every one of those rows' route
+    # blocks get none, and dq of the other rows is exactly zero
+    d_o2 = torch.zeros_like(d_o)
+    d_o2[:, :, 800:] = d_o[:, :, 800:]
+    dq, dk, dv = bsa.backward(q, k, v, o, d_o2, lse, rp, ci, w.block)
+    torch.cuda.synchronize()
+    assert (dq[:, :, :800] == 0).all()
+
+
+def test_backward_errors():
+    q = torch.zeros(1, 2, 128, 64, dtype=torch.float32, device="cuda")
+    rp, ci = bsa.build_route(bsa.route_spec(R.BF1), 128, 64)
+    trp, tci = bsa.build_route_transpose(rp, ci)
+    lse = torch.zeros(1, 2, 128, device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_backward(q, q, q, q, q, lse, q.clone(), q.clone(), q.clone(), rp, ci, trp, tci, 64, ws)
+    assert e.value.status == bsa.BSA_ERR_UNSUPPORTED
+    qb = q.to(torch.bfloat16)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_backward(qb, qb, qb, qb, qb, lse, qb.clone(), qb.clone(), qb.clone(), rp, ci, trp, tci, 64, small)
+    assert e.value.status == bsa.BSA_ERR_CAPACITY
