@@ -15,7 +15,7 @@ on the launch stream, bracketed by torch.cuda.synchronize().  Separately timed o
 inputs: the forward alone (the dominant kernel, for the roofline), and the same kernel over the
 dense causal route (the speedup denominator), in both orders sparse->dense and dense->sparse.
 
-Also reported, outside the timed region: selected-page decode of the newest token over the same
+Also reported, outside the timed region: the backward pass (BF1 and dense route), selected-page decode of the newest token over the same
 tensors as a key/value cache (batch 1 and 16; persistent plan, plan per token, dense route), the
 topology sweep (BF1 against the local sliding band
 and the static-random graph at the nearest selected-pair count, same inputs, with each graph's
@@ -238,6 +238,39 @@ def decode_bench(w, kd, vd, steps: int, batch: int = 1) -> dict:
     return out
 
 
+def backward_bench(w, qd, kd, vd, steps: int) -> dict:
+    """The gradients (bsa_backward) of the workload's forward, BF1 route and dense causal route,
+    with the transposed route built once.  FLOPs use the usual count for attention gradients,
+    2.5x the forward's (five products of 2*d flops per selected pair: the recomputed scores, dP,
+    dQ, dK, dV); the kernels also recompute the scores and dP once more (seven products)."""
+    import torch
+    import long_context_block_amd as bsa
+    g = torch.Generator(device=qd.device).manual_seed(11)
+    d_o = torch.randn(qd.shape, device=qd.device, generator=g).to(qd.dtype)
+    out = {}
+    for name, kind in (("bf1", w.route_kind), ("dense_causal", bsa.BSA_ROUTE_DENSE_CAUSAL)):
+        spec = bsa.route_spec(kind, w.n_local, w.keep_first, w.n_random, w.route_seed)
+        rp, ci = bsa.build_route(spec, w.n, w.block)
+        trp, tci = bsa.build_route_transpose(rp, ci)
+        o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, with_lse=True)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        nbytes = bsa.bsa_backward_workspace_bytes(w.batch, w.heads_q, w.heads_kv, w.n, w.d, w.block, ci.numel())
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=qd.device)
+        torch.cuda.synchronize()
+        S = selected_pairs(rp.cpu().numpy(), ci.cpu().numpy(), w.n, w.block)
+        fn = lambda: bsa.bsa_backward(qd, kd, vd, o, d_o, lse, dq, dk, dv, rp, ci, trp, tci, w.block, ws)  # noqa: E731
+        ms = time_loop(fn, max(5, steps // (1 if name == "bf1" else 10)), 2)
+        flops = 10.0 * w.d * w.batch * w.heads_q * S
+        out[name] = {"ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "roofline": {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+                     "workspace_bytes": int(nbytes)}
+        del ws, dq, dk, dv, o, lse
+        torch.cuda.empty_cache()
+    out["speedup_vs_dense"] = round(out["dense_causal"]["ms"] / out["bf1"]["ms"], 3)
+    return out
+
+
 def algorithmic_bytes(w) -> int:
     """Q, K, V read once and O written once, in the workload's dtype."""
     e = 4 if w.dtype == "fp32" else 2
@@ -452,6 +485,7 @@ def main():
     if not args.no_others:
         out["topology_sweep"] = topology_sweep(w, qd, kd, vd, args.steps)
         out["decode"] = [decode_bench(w, kd, vd, args.steps, batch) for batch in (1, 16)]
+        out["backward"] = backward_bench(w, qd, kd, vd, args.steps)
         out["other_workloads"] = other_workloads([x for x in synth.WORKLOADS if x != w.name], args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)

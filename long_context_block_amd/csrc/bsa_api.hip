@@ -251,7 +251,8 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
     if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
     const int64_t nqb = (n + block - 1) / block;
     const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
-    if ((int64_t)batch * heads_kv * segs > INT32_MAX || (int64_t)batch * heads_q * nqb > INT32_MAX)
+    if ((int64_t)batch * heads_kv * segs > INT32_MAX || (int64_t)batch * heads_q * nqb > INT32_MAX ||
+        (int64_t)batch * heads_kv * nqb * 16 > INT32_MAX)
         return fail(BSA_ERR_UNSUPPORTED, "grid too large");
     bsa::BwdParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.d_o = d_o; p.lse = lse;

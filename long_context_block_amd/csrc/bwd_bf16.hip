@@ -469,32 +469,49 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// Sum the segments of key blocks split over several work-groups, in segment order.
+// Sum the segments of key blocks split over several work-groups, in segment order.  Work-group
+// (b, kv head, j, part) takes 1024 consecutive elements of the block's dK and dV (one float4 of
+// each per thread); the segment loop is unrolled so that its loads are in flight together.
+constexpr int kRedElems = 1024;
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
-    const int64_t bg = blockIdx.x / p.nqb;
-    const int64_t j = blockIdx.x % p.nqb;
+    constexpr int PARTS = BLK * D / kRedElems;
+    const int64_t w = blockIdx.x;
+    const int part = (int)(w % PARTS);
+    const int64_t j = (w / PARTS) % p.nqb;
+    const int64_t bg = w / PARTS / p.nqb;
     // (clamped to the workspace's segment slots, so that even a malformed route stays in bounds)
     const int s1 = p.seg_ptr[j + 1] < p.nseg_ub ? p.seg_ptr[j + 1] : (int)p.nseg_ub;
     const int s0 = p.seg_ptr[j] < s1 ? p.seg_ptr[j] : s1;
     if (s1 - s0 < 2) return;
     const int64_t n = p.n;
-    for (int e = threadIdx.x * 4; e < BLK * D; e += 256 * 4) {
-        const int r = e / D, c = e % D;
-        const int64_t krow = j * BLK + r;
-        if (krow >= n) continue;
-        float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
-        for (int sgi = s0; sgi < s1; ++sgi) {
-            const float* part = p.part + ((bg * p.nseg_ub + sgi) * 2) * BLK * D;
-            const float4 a = *(const float4*)(part + e), v = *(const float4*)(part + BLK * D + e);
-            sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
-            sv.x += v.x; sv.y += v.y; sv.z += v.z; sv.w += v.w;
+    const int e = part * kRedElems + threadIdx.x * 4;
+    const int r = e / D, c = e % D;
+    const int64_t krow = j * BLK + r;
+    if (krow >= n) return;
+    const float* base = p.part + (bg * p.nseg_ub) * 2 * BLK * D + e;
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+    constexpr int U = 8;
+    for (int s = s0; s < s1; s += U) {
+        float4 a[U], v[U];
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            const int sg = s + x < s1 ? s + x : s1 - 1;
+            a[x] = *(const float4*)(base + (int64_t)sg * 2 * BLK * D);
+            v[x] = *(const float4*)(base + (int64_t)sg * 2 * BLK * D + BLK * D);
         }
-        __bf16* Dk = (__bf16*)p.dk + (bg * n + krow) * D + c;
-        __bf16* Dv = (__bf16*)p.dv + (bg * n + krow) * D + c;
-        *(uint2*)Dk = make_uint2(pack_bf16x2(sk.x * p.scale, sk.y * p.scale), pack_bf16x2(sk.z * p.scale, sk.w * p.scale));
-        *(uint2*)Dv = make_uint2(pack_bf16x2(sv.x, sv.y), pack_bf16x2(sv.z, sv.w));
+#pragma unroll
+        for (int x = 0; x < U; ++x) {
+            if (s + x < s1) {
+                sk.x += a[x].x; sk.y += a[x].y; sk.z += a[x].z; sk.w += a[x].w;
+                sv.x += v[x].x; sv.y += v[x].y; sv.z += v[x].z; sv.w += v[x].w;
+            }
+        }
     }
+    __bf16* Dk = (__bf16*)p.dk + (bg * n + krow) * D + c;
+    __bf16* Dv = (__bf16*)p.dv + (bg * n + krow) * D + c;
+    *(uint2*)Dk = make_uint2(pack_bf16x2(sk.x * p.scale, sk.y * p.scale), pack_bf16x2(sk.z * p.scale, sk.w * p.scale));
+    *(uint2*)Dv = make_uint2(pack_bf16x2(sv.x, sv.y), pack_bf16x2(sv.z, sv.w));
 }
 
 template <int D, int BLK>
@@ -512,8 +529,9 @@ hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, BLK>), dim3((unsigned)((int64_t)p.batch * p.heads_kv * p.nseg_ub)),
                        dim3(BLK / 32 * 64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D, BLK>), dim3((unsigned)((int64_t)p.batch * p.heads_kv * p.nqb)),
-                       dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D, BLK>),
+                       dim3((unsigned)((int64_t)p.batch * p.heads_kv * p.nqb * (BLK * D / kRedElems))), dim3(256), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
