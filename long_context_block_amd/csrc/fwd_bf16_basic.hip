@@ -11,8 +11,9 @@
 // How: one work-group per work item (batch, GP query heads sharing a key/value head, query
 // block i), GP * BLK/32 wavefronts of 32 query rows each; K/V chunks of CK keys are copied
 // HBM -> LDS one chunk ahead (global_load_lds_dwordx4) into a two-stage ring with one barrier
-// per chunk; each 64-key step computes S^T = K Q^T on the matrix cores, the online softmax in
-// registers (one query per lane), and O^T += V^T P^T with V^T read by the LDS transposing read.
+// per chunk; each softmax step (64 keys, or 32 with 32-key chunks) computes S^T = K Q^T on the
+// matrix cores, the online softmax in registers (one query per lane), and O^T += V^T P^T with
+// V^T read by the LDS transposing read.
 // The steps of a wavefront run in sequence; the two wavefronts of a SIMD overlap each other.
 
 #include "fwd_common.hpp"
@@ -40,13 +41,15 @@ struct CfgBasic {
     static constexpr int NW = NWQ * GP;               // wavefronts per work-group
     static constexpr int NT = NW * 64;                // threads per work-group
     static constexpr int CPT = BLK / CK;              // LDS chunks per key block
-    static constexpr int SPC = CK / KC;               // 64-key softmax steps per chunk
+    static constexpr int NC2 = CK >= 64 ? 2 : 1;      // 32-key score accumulators per softmax step
+    static constexpr int KS = 32 * NC2;               // keys per softmax step
+    static constexpr int SPC = CK / KS;               // softmax steps per chunk
     static constexpr int KCH = D / 8;                 // 16-byte chunks per K/V row
     static constexpr int NI = CK * D / 8 / 64;        // 1 KiB direct-to-LDS loads per chunk and tensor
     static constexpr int NI_W = NI / NW;              // ... per wavefront
     static constexpr int NST = 2;                     // ring stages
     static_assert(NI_W * NW == NI, "chunk split");
-    static_assert(CPT * CK == BLK && SPC * KC == CK, "chunking");
+    static_assert(CPT * CK == BLK && SPC * KS == CK, "chunking");
 };
 
 template <int D, int BLK, int GP, int CK>
@@ -139,17 +142,17 @@ void fwd_bf16_basic_kernel(FwdParams p) {
     auto scores = [&](const __bf16* Ks, int krow0, bool masked, int lim, uint32_t (&pk)[2][8]) {
         f32x16 sacc[2];
         sacc[0] = f32x16{};
-        sacc[1] = f32x16{};
+        sacc[1] = f32x16{};  // (only the first NC2 are used)
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
+            for (int c2 = 0; c2 < C::NC2; ++c2) {
                 const bf16x8 a = *(const bf16x8*)(Ks + Z::k_off(krow0 + 32 * c2 + l32, 2 * kk + hf));
                 sacc[c2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[c2], 0, 0, 0);
             }
         if (masked) {  // only the diagonal block (or a skipped entry) masks anything (uniform)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
+            for (int c2 = 0; c2 < C::NC2; ++c2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = 32 * c2 + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -158,7 +161,7 @@ void fwd_bf16_basic_kernel(FwdParams p) {
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < C::NC2; ++c2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[c2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -174,7 +177,7 @@ void fwd_bf16_basic_kernel(FwdParams p) {
         const float mo = (m_run == -INFINITY) ? 0.0f : m_run;  // fully masked so far: weights 0
         // P = exp2(s * scale*log2e - m), packed to bf16; row sums of the rounded P
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < C::NC2; ++c2)
 #pragma unroll
             for (int x = 0; x < 8; ++x) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[c2][2 * x], p.scale_log2, -mo));
@@ -183,10 +186,10 @@ void fwd_bf16_basic_kernel(FwdParams p) {
                 l_run = dot2_bf16_ones(pk[c2][x], l_run);
             }
     };
-    // ---- O^T[d][query] += V^T[d][key] P^T[key][query] over one chunk ---------------------
+    // ---- O^T[d][query] += V^T[d][key] P^T[key][query] over one softmax step -------------
     auto pv = [&](const __bf16* Vs, int vrow0, const uint32_t (&pk)[2][8]) {
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int c2 = 0; c2 < C::NC2; ++c2)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const bf16x8 bop = __builtin_bit_cast(
@@ -223,10 +226,10 @@ void fwd_bf16_basic_kernel(FwdParams p) {
             if (ch + 1 < NCH) issue(chunk_row(((ch + 1) / C::CPT == t) ? jt : jt1, ch + 1), st ^ 1);
 #pragma unroll
             for (int sp = 0; sp < C::SPC; ++sp) {
-                const int kb = CK * part + KC * sp;  // first key of this step within the block
-                const int lim = (jt < 0) ? -1 : (jt == i ? qloc - kb : KC);
-                scores(sK[st], KC * sp, jt < 0 || jt == i, lim, pk);
-                pv(sV[st], KC * sp, pk);
+                const int kb = CK * part + C::KS * sp;  // first key of this step within the block
+                const int lim = (jt < 0) ? -1 : (jt == i ? qloc - kb : C::KS);
+                scores(sK[st], C::KS * sp, jt < 0 || jt == i, lim, pk);
+                pv(sV[st], C::KS * sp, pk);
             }
             st ^= 1;
         }
@@ -263,6 +266,9 @@ template <int D, int BLK>
 hipError_t launch_basic_gp(const FwdParams& p, hipStream_t stream) {
     const int G = p.heads_q / p.heads_kv;
     if (G % 2 == 0) return launch_basic<D, BLK, 2, (BLK < kChunkGqa ? BLK : kChunkGqa)>(p, stream);
+    // 64-token blocks without a GQA pair: 32-key chunks halve the LDS ring (32 KiB at d = 128),
+    // so twice as many of these short, latency-bound work-groups are resident per CU
+    if (BLK == 64) return launch_basic<D, BLK, 1, 32>(p, stream);
     return launch_basic<D, BLK, 1, 64>(p, stream);
 }
 

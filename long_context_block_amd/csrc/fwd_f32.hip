@@ -22,9 +22,9 @@ constexpr int kKeyChunk = 32;
 template <int D, int BLK>
 __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
     constexpr int TPR = kF32Threads / BLK;  // threads per query row
-    constexpr int DPT = D / TPR;            // output dims per thread (strided by TPR)
-    __shared__ float Kc[kKeyChunk][D];
-    __shared__ float Vc[kKeyChunk][D];
+    constexpr int DPT = D / TPR;            // output dims per thread (contiguous, read as float4)
+    __shared__ __attribute__((aligned(16))) float Kc[kKeyChunk][D];
+    __shared__ __attribute__((aligned(16))) float Vc[kKeyChunk][D];
 
     const int tid = threadIdx.x;
     const int64_t nqb = p.nqb;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
     float q[DPT], acc[DPT];
 #pragma unroll
     for (int x = 0; x < DPT; ++x) {
-        q[x] = row_ok ? Q[t * D + sub + TPR * x] : 0.f;
+        q[x] = row_ok ? Q[t * D + sub * DPT + x] : 0.f;
         acc[x] = 0.f;
     }
     float m_run = -INFINITY, l_run = 0.f;
@@ -61,11 +61,12 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
         const bool diag = (j == i);
         for (int kc = 0; kc < BLK; kc += kKeyChunk) {
             __syncthreads();  // previous chunk fully consumed
-            for (int x = tid; x < kKeyChunk * D; x += kF32Threads) {
-                const int r = x / D, c = x % D;
+            for (int x = tid; x < kKeyChunk * D / 4; x += kF32Threads) {
+                const int r = x / (D / 4), c = 4 * (x % (D / 4));
                 const int64_t s = j * BLK + kc + r;
-                Kc[r][c] = (s < p.n) ? K[s * D + c] : 0.f;
-                Vc[r][c] = (s < p.n) ? V[s * D + c] : 0.f;
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                *(float4*)&Kc[r][c] = (s < p.n) ? *(const float4*)&K[s * D + c] : z;
+                *(float4*)&Vc[r][c] = (s < p.n) ? *(const float4*)&V[s * D + c] : z;
             }
             __syncthreads();
             float sc[kKeyChunk];
@@ -74,7 +75,13 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
             for (int r = 0; r < kKeyChunk; ++r) {
                 float part = 0.f;
 #pragma unroll
-                for (int x = 0; x < DPT; ++x) part = fmaf(q[x], Kc[r][sub + TPR * x], part);
+                for (int x = 0; x < DPT; x += 4) {
+                    const float4 kv = *(const float4*)&Kc[r][sub * DPT + x];
+                    part = fmaf(q[x], kv.x, part);
+                    part = fmaf(q[x + 1], kv.y, part);
+                    part = fmaf(q[x + 2], kv.z, part);
+                    part = fmaf(q[x + 3], kv.w, part);
+                }
 #pragma unroll
                 for (int o = 1; o < TPR; o <<= 1) part += __shfl_xor(part, o);
                 float s2 = part * p.scale_log2;
@@ -94,14 +101,20 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
                 const float pr = exp2f(sc[r] - m_run);
                 l_run += pr;
 #pragma unroll
-                for (int x = 0; x < DPT; ++x) acc[x] = fmaf(pr, Vc[r][sub + TPR * x], acc[x]);
+                for (int x = 0; x < DPT; x += 4) {
+                    const float4 vv = *(const float4*)&Vc[r][sub * DPT + x];
+                    acc[x] = fmaf(pr, vv.x, acc[x]);
+                    acc[x + 1] = fmaf(pr, vv.y, acc[x + 1]);
+                    acc[x + 2] = fmaf(pr, vv.z, acc[x + 2]);
+                    acc[x + 3] = fmaf(pr, vv.w, acc[x + 3]);
+                }
             }
         }
     }
     if (row_ok) {
         const float inv = 1.f / l_run;
 #pragma unroll
-        for (int x = 0; x < DPT; ++x) O[t * D + sub + TPR * x] = acc[x] * inv;
+        for (int x = 0; x < DPT; ++x) O[t * D + sub * DPT + x] = acc[x] * inv;
         if (p.lse && sub == 0) p.lse[bh * p.n + t] = (m_run + log2f(l_run)) * 0.69314718055994530942f;
     }
 }
