@@ -104,7 +104,7 @@ bsa_status validate_forward(const void* q, const void* k, const void* v, void* o
     }
     const int G = heads_q / heads_kv;
     const int gp = (dtype == BSA_BF16 && G % 2 == 0) ? 2 : 1;
-    const int64_t wg = (int64_t)batch * (heads_q / gp) * nqb;
+    const int64_t wg = (int64_t)batch * (heads_q / gp) * nqb * (dtype == BSA_FP32 ? (block + 15) / 16 : 1);
     if (wg > INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "grid of %lld work-groups too large", (long long)wg);
     return ok();
 }

@@ -1,6 +1,6 @@
 // fwd_f32.hip — float32 block-sparse attention forward (VALU FMA, fp32 throughout).
 //
-// One work-group per (batch, query head, query block i).  The work-group walks row i of the
+// One work-group per (batch, query head, 16 rows of query block i).  The work-group walks row i of the
 // CSR route ("Block Sparse Attention in LLMs", section 6: for each query block, for each
 // allowed key block), stages keys/values through LDS in chunks of 32 keys and keeps an online
 // softmax per query row ("Block Sparse Attention in LLMs", section 7: tile the computation and
@@ -12,24 +12,29 @@
 // scale*log2(e).
 
 #include "bsa_internal.hpp"
+#include "lane_ops.hpp"
 
 namespace bsa {
 namespace {
 
 constexpr int kF32Threads = 256;
 constexpr int kKeyChunk = 32;
+constexpr int kRows = 16;  // query rows per work-group: 16 threads per row
 
 template <int D, int BLK>
 __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
-    constexpr int TPR = kF32Threads / BLK;  // threads per query row
-    constexpr int DPT = D / TPR;            // output dims per thread (contiguous, read as float4)
+    constexpr int TPR = kF32Threads / kRows;  // threads per query row (one DPP row of lanes)
+    constexpr int DPT = D / TPR;              // output dims per thread (contiguous, read as float4)
+    constexpr int PARTS = BLK / kRows;        // work-groups per query block
     __shared__ __attribute__((aligned(16))) float Kc[kKeyChunk][D];
     __shared__ __attribute__((aligned(16))) float Vc[kKeyChunk][D];
 
     const int tid = threadIdx.x;
     const int64_t nqb = p.nqb;
-    const int64_t bh = blockIdx.x / nqb;               // batch * heads_q + h
-    const int64_t i = nqb - 1 - (blockIdx.x % nqb);    // longest rows first (routes grow with i)
+    const int rpart = blockIdx.x % PARTS;
+    const int64_t wi = blockIdx.x / PARTS;
+    const int64_t bh = wi / nqb;               // batch * heads_q + h
+    const int64_t i = nqb - 1 - (wi % nqb);    // longest rows first (routes grow with i)
     const int64_t b = bh / p.heads_q;
     const int64_t h = bh % p.heads_q;
     const int64_t kvh = h / (p.heads_q / p.heads_kv);
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
     const float* V = (const float*)p.v + (b * p.heads_kv + kvh) * p.n * D;
     float* O = (float*)p.o + (b * p.heads_q + h) * p.n * D;
 
-    const int rloc = tid / TPR;  // query row within the block
+    const int rloc = rpart * kRows + tid / TPR;  // query row within the block
     const int sub = tid % TPR;
     const int64_t t = i * BLK + rloc;
     const bool row_ok = t < p.n;
@@ -82,8 +87,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
                     part = fmaf(q[x + 2], kv.z, part);
                     part = fmaf(q[x + 3], kv.w, part);
                 }
-#pragma unroll
-                for (int o = 1; o < TPR; o <<= 1) part += __shfl_xor(part, o);
+                part = lanes::group_sum<TPR>(part);
                 float s2 = part * p.scale_log2;
                 if (diag && (kc + r > rloc)) s2 = -INFINITY;  // causal mask inside the diagonal block
                 sc[r] = s2;
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
 
 template <int D, int BLK>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-    const int64_t grid = (int64_t)p.batch * p.heads_q * p.nqb;
+    const int64_t grid = (int64_t)p.batch * p.heads_q * p.nqb * (BLK / kRows);
     hipLaunchKernelGGL((fwd_f32_kernel<D, BLK>), dim3((unsigned)grid), dim3(kF32Threads), 0, stream, p);
     return hipGetLastError();
 }
