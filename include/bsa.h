@@ -176,7 +176,8 @@ size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block);
  * [batch, heads_q, n] from bsa_forward (required); the route (row_ptr, col_idx, nnz) and its
  * transpose from bsa_build_route_transpose (t_row_ptr, t_col_idx).  Outputs: dq like q, dk and
  * dv like k and v, in `dtype`.  workspace: float32 scratch of at least
- * bsa_backward_workspace_bytes(...) bytes (D, the segment table of the transposed rows, and fp32
+ * bsa_backward_workspace_bytes(...) bytes (D and lse scaled to base 2 over rows padded to whole
+ * blocks, the segment table of the transposed rows, and fp32
  * partial dk/dv of key blocks whose readers are split over several work-groups); its contents
  * on entry do not matter.  Supported: dtype BF16; d in {64, 128}; block in {64, 128}; any n >= 0.
  * Five kernels on `stream`; the result is deterministic (no atomics).

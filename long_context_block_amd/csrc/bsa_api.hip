@@ -227,7 +227,8 @@ size_t bsa_backward_workspace_bytes(int32_t batch, int32_t heads_q, int32_t head
         return 0;
     const int64_t nqb = (n + block - 1) / block;
     const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
-    return align256((size_t)batch * heads_q * n * sizeof(float)) + align256((size_t)(nqb + 1) * sizeof(int32_t)) +
+    return align256((size_t)2 * batch * heads_q * nqb * block * sizeof(float)) + 256 +
+           align256((size_t)(nqb + 1) * sizeof(int32_t)) +
            (size_t)batch * heads_kv * segs * 2 * block * d * sizeof(float);
 }
 
@@ -251,6 +252,7 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
     if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
     const int64_t nqb = (n + block - 1) / block;
     const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
+    if (nqb * block > INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "n=%lld too large for the backward", (long long)n);
     if ((int64_t)batch * heads_kv * segs > INT32_MAX || (int64_t)batch * heads_q * nqb > INT32_MAX ||
         (int64_t)batch * heads_kv * nqb * 16 > INT32_MAX)
         return fail(BSA_ERR_UNSUPPORTED, "grid too large");
@@ -259,13 +261,17 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
     p.dq = dq; p.dk = dk; p.dv = dv;
     p.row_ptr = row_ptr; p.col_idx = col_idx; p.t_row_ptr = t_row_ptr; p.t_col_idx = t_col_idx;
     char* ws = (char*)workspace;
+    const int64_t n_pad = nqb * block;
     p.dvec = (float*)ws;
-    ws += align256((size_t)batch * heads_q * n * sizeof(float));
+    p.lse2 = p.dvec + (size_t)batch * heads_q * n_pad;
+    ws += align256((size_t)2 * batch * heads_q * n_pad * sizeof(float));
+    p.ld_pad = (float*)ws;
+    ws += 256;
     p.seg_ptr = (int32_t*)ws;
     ws += align256((size_t)(nqb + 1) * sizeof(int32_t));
     p.part = (float*)ws;
     p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv;
-    p.nqb = (int32_t)nqb; p.n = n; p.nnz = nnz; p.nseg_ub = segs;
+    p.nqb = (int32_t)nqb; p.n = n; p.n_pad = n_pad; p.nnz = nnz; p.nseg_ub = segs;
     const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
     p.scale = (float)sc;
     p.scale_log2 = (float)(sc * 1.4426950408889634073599);

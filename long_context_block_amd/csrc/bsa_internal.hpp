@@ -98,12 +98,15 @@ struct BwdParams {
     const int32_t* col_idx;
     const int32_t* t_row_ptr;  // transposed route: query blocks reading key block j
     const int32_t* t_col_idx;
-    float* dvec;      // workspace: D = rowsum(dO * O) [batch, heads_q, n]
+    float* dvec;      // workspace: D = rowsum(dO * O) [batch, heads_q, n_pad], 0 past n
+    float* lse2;      // workspace: lse * log2(e) [batch, heads_q, n_pad], +inf past n
+    float* ld_pad;    // workspace: 32 x +inf, then 32 x 0: lse2 and D of a fully excluded row run
     int32_t* seg_ptr; // workspace: [nqb + 1] segment prefix of the transposed rows
     float* part;      // workspace: [batch * heads_kv * nseg_ub, 2, block, d] partial dK, dV
     int32_t batch, heads_q, heads_kv;
     int32_t nqb;
     int64_t n;
+    int64_t n_pad;    // n rounded up to a whole block
     int64_t nnz;
     int64_t nseg_ub;  // segments per (batch, kv head), upper bound
     float scale;

@@ -27,15 +27,19 @@ namespace {
 
 using namespace bwd;
 
-// ---- D = rowsum(dO * O) -------------------------------------------------------------------------
+// ---- D = rowsum(dO * O), lse * log2(e) -----------------------------------------------------------
+// Both over rows padded to whole blocks: past n, D = 0 and lse2 = +inf, so that a padded query
+// row has P = exp2(s - lse2) = 0 without a mask.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
-    const int64_t rows = (int64_t)p.batch * p.heads_q * p.n;
-    const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int64_t prow = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;  // padded row
     const int c = threadIdx.x % LPR;
+    const int64_t bh = prow / p.n_pad, t = prow % p.n_pad;
+    const bool in = bh < (int64_t)p.batch * p.heads_q;
+    const int64_t row = bh * p.n + t;
     float s = 0.f;
-    if (row < rows) {
+    if (in && t < p.n) {
         const uint4 a = *(const uint4*)((const __bf16*)p.d_o + row * D + c * 8);
         const uint4 o = *(const uint4*)((const __bf16*)p.o + row * D + c * 8);
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
@@ -47,7 +51,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-    if (row < rows && c == 0) p.dvec[row] = s;
+    if (in && c == 0) {
+        p.dvec[prow] = s;
+        p.lse2[prow] = t < p.n ? p.lse[row] * kLog2e : __builtin_inff();
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 64) p.ld_pad[threadIdx.x] = threadIdx.x < 32 ? __builtin_inff() : 0.f;
 }
 
 // ---- dQ --------------------------------------------------------------------------------------
@@ -85,7 +93,7 @@ void bwd_dq_kernel(BwdParams p) {
         }
     }
     const float lse2 = row_ok ? p.lse[bh * n + qrow] * kLog2e : 0.f;
-    const float dval = row_ok ? p.dvec[bh * n + qrow] : 0.f;
+    const float dval = row_ok ? p.dvec[bh * p.n_pad + qrow] : 0.f;
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(1024) void bwd_seg_kernel(BwdParams p, int cpb) {
 
 template <int D, int BLK>
 hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.batch * p.heads_q * p.n;
+    const int64_t rows = (int64_t)p.batch * p.heads_q * p.n_pad;
     const int64_t prep_blocks = (rows * (D / 8) + 255) / 256;
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();

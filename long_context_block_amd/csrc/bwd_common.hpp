@@ -63,13 +63,35 @@ __device__ inline void issue_tile(const __bf16* M, int64_t row0, int64_t last, _
     }
 }
 
-// One dword per lane of wavefront 0 into LDS: dst[lane] = *src (global_load_lds_dword).
-__device__ inline void issue_dword(const float* src, float* dst, int wv) {
+// The same copy into the LDS byte address `lds` (wavefront-uniform) of the tile.
+template <int D, int NW, int ROWS>
+__device__ inline void issue_tile_at(const __bf16* M, int64_t row0, int64_t last, uint32_t lds, int wv, int lane) {
+    constexpr int NI = ROWS * D / 512;
+    constexpr int NI_W = NI / NW;
+    static_assert(NI_W * NW == NI, "tile split");
+    const int64_t b = row0 < last ? row0 : last;
+    const int delta = (int)(row0 - b), lim = (int)(last - b);
+    const char* base = (const char*)(M + b * D);
+#pragma unroll
+    for (int u = 0; u < NI_W; ++u) {
+        const int qi = wv * NI_W + u;
+        const int P = 64 * qi + lane;
+        const int r = P / Sw2<D>::KCH, pc = P % Sw2<D>::KCH;
+        const int rr = (r + delta) < lim ? (r + delta) : lim;
+        copy16_to_lds(base, (uint32_t)(rr * D * 2 + ((pc ^ Sw2<D>::f(r)) << 4)), lds + 1024u * qi);
+    }
+}
+
+// One dword per lane of wavefront 0 into LDS: dword `lane` at LDS byte address lds = *src
+// (global_load_lds_dword).
+__device__ inline void issue_dword_at(const float* src, uint32_t lds, int wv) {
     if (wv != 0) return;
-    const uint32_t lb = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)dst;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lb)),
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
                  "v"(src)
                  : "memory");
+}
+__device__ inline void issue_dword(const float* src, float* dst, int wv) {
+    issue_dword_at(src, (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)dst, wv);
 }
 
 // Copy kCh floats v[row0 .. row0 + kCh) (indices clamped to last) into LDS.

@@ -48,11 +48,14 @@ __global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(1
 void bwd_dkdv_kernel(BwdParams p) {
     constexpr int NW = BLK / 32;
     constexpr int UPB = BLK / kCh;  // 64-query units per query block
-    __shared__ __attribute__((aligned(1024))) __bf16 sQ[NST][kSub * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 sO[NST][kSub * D];  // dO
-    __shared__ __attribute__((aligned(16))) float sLD[NST][2 * kSub];   // lse of 32 rows, then D
+    // stage st: tile [st][0] = Q rows, [st][1] = dO rows of one sub-chunk
+    __shared__ __attribute__((aligned(1024))) __bf16 sT[NST][2][kSub * D];
+    // lse2 of 32 rows, then D; one copy per wavefront, so that all wavefronts issue the same loads
+    __shared__ __attribute__((aligned(16))) float sLD[NST][NW][2 * kSub];
+    constexpr uint32_t TILE = kSub * D * 2, STAGE = 2 * TILE, LDSTAGE = NW * 2 * kSub * 4;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t bg = blockIdx.x / p.nseg_ub;  // batch * heads_kv + g
     const int sw = (int)(blockIdx.x % p.nseg_ub);
     const int64_t nqb = p.nqb;
@@ -63,24 +66,64 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int64_t mid = (lo + hi + 1) >> 1;
         if (p.seg_ptr[mid] <= sw) lo = mid; else hi = mid - 1;
     }
-    const int64_t j = lo;
+    const int j = (int)lo;
     const int seg = sw - p.seg_ptr[j];
     const int nseg = p.seg_ptr[j + 1] - p.seg_ptr[j];
     const int64_t b = bg / p.heads_kv, g = bg % p.heads_kv;
     const int G = p.heads_q / p.heads_kv;
-    const int64_t n = p.n;
+    const int64_t n = p.n, n_pad = p.n_pad;
 
     int64_t t0 = p.t_row_ptr[j], t1 = p.t_row_ptr[j + 1];
     t0 = t0 < 0 ? 0 : (t0 > p.nnz ? p.nnz : t0);
     t1 = t1 < t0 ? t0 : (t1 > p.nnz ? p.nnz : t1);
-    const int units_all = (int)(t1 - t0) * G * UPB;
+    const int upt = G * UPB;  // units per entry of the transposed row
+    const int units_all = (int)(t1 - t0) * upt;
     const int u_begin = seg * kSeg;
     const int u_end = (u_begin + kSeg < units_all) ? u_begin + kSeg : units_all;
     const int NSUB = u_end > u_begin ? 2 * (u_end - u_begin) : 0;
 
+    // Sub-chunk table: lane x describes sub-chunks x (index 0) and 64 + x (index 1) by batch *
+    // query head, first query row, and kind: the row's offset within the diagonal block
+    // (0 .. BLK - 1), BLK off the diagonal, -1 for an entry that is no causal reader of j.
+    static_assert(2 * kSeg <= 128, "two sub-chunks per lane");
+    int tbh[2], tq0[2], tkind[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int x = 64 * h + lane;
+        tbh[h] = 0;
+        tq0[h] = 0;
+        tkind[h] = -1;
+        if (x < NSUB) {
+            const int u = u_begin + (x >> 1);
+            const int ti = u / upt, rem = u - ti * upt;
+            const int iq = p.t_col_idx[t0 + ti];
+            const bool bad = iq < j || iq >= nqb;
+            const int i = bad ? j : iq;
+            tbh[h] = (int)(b * p.heads_q + g * G) + rem / UPB;
+            tq0[h] = i * BLK + kCh * (rem % UPB) + kSub * (x & 1);
+            tkind[h] = bad ? -1 : (i == j ? tq0[h] - j * BLK : BLK);
+        }
+    }
+    auto fetch = [&](const int(&tab)[2], int x) {
+        const int a = __builtin_amdgcn_readlane(tab[0], x & 63), c = __builtin_amdgcn_readlane(tab[1], x & 63);
+        return x < 64 ? a : c;
+    };
+    // Sub-chunks on the diagonal block need the causal mask.  When they form a prefix of the
+    // segment (the transposed rows list query blocks in increasing order, so the diagonal entry
+    // comes first), only that prefix runs the masked step; otherwise every sub-chunk does.
+    int NM;
+    {
+        const uint64_t m0 = __builtin_amdgcn_ballot_w64(tkind[0] >= 0 && tkind[0] < BLK);
+        const uint64_t m1 = __builtin_amdgcn_ballot_w64(tkind[1] >= 0 && tkind[1] < BLK);
+        const int c0 = __builtin_popcountll(m0), c1 = __builtin_popcountll(m1);
+        auto prefix = [](int c) { return c >= 64 ? ~0ull : ((1ull << c) - 1); };
+        const bool pre = (m0 == prefix(c0)) && (c0 == 64 ? m1 == prefix(c1) : m1 == 0);
+        NM = pre ? c0 + c1 : NSUB;
+    }
+
     // this wavefront's 32 keys, resident as B operands: K[key][16kk + 8hf ..], V likewise
     const int kloc = 32 * wv + l32;
-    const int64_t krow = j * BLK + kloc;
+    const int64_t krow = (int64_t)j * BLK + kloc;
     const bool key_ok = krow < n;
     bf16x8 kf[D / 16], vf[D / 16];
     {
@@ -99,61 +142,76 @@ void bwd_dkdv_kernel(BwdParams p) {
         dv[db] = f32x16{};
     }
 
-    // sub-chunk x of the segment -> (query block i, batch * query head, first query row)
-    auto locate = [&](int x, int64_t& i, int64_t& bh, int64_t& q0) {
-        const int u = u_begin + (x >> 1);
-        const int ti = u / (G * UPB), rem = u % (G * UPB);
-        const int64_t iq = __builtin_amdgcn_readfirstlane(((cptr)p.t_col_idx)[t0 + ti]);
-        i = (iq < j || iq >= nqb) ? -1 : iq;  // malformed: a fully masked sub-chunk
-        bh = b * p.heads_q + g * G + rem / UPB;
-        q0 = (i >= 0 ? i : j) * BLK + kCh * (rem % UPB) + kSub * (x & 1);
-    };
+    const uint32_t lds_t = lds_addr(&sT[0][0][0]);
+    const uint32_t lds_ld = (uint32_t)(uintptr_t)(const lds_void*)&sLD[0][0];
     auto issue = [&](int x, int st) {
-        int64_t i, bh, q0;
-        locate(x, i, bh, q0);
-        issue_tile<D, NW, kSub>((const __bf16*)p.q + bh * n * D, q0, n - 1, sQ[st], wv, lane);
-        issue_tile<D, NW, kSub>((const __bf16*)p.d_o + bh * n * D, q0, n - 1, sO[st], wv, lane);
-        int64_t r = q0 + (lane & 31);
-        r = r < n - 1 ? r : n - 1;
-        issue_dword((hf ? p.dvec : p.lse) + bh * n + r, sLD[st], wv);
+        const int bh = fetch(tbh, x), q0 = fetch(tq0, x), kind = fetch(tkind, x);
+        const int64_t r0 = (int64_t)bh * n, last = r0 + n - 1;
+        issue_tile_at<D, NW, kSub>((const __bf16*)p.q, r0 + q0, last, lds_t + st * STAGE, wv, lane);
+        issue_tile_at<D, NW, kSub>((const __bf16*)p.d_o, r0 + q0, last, lds_t + st * STAGE + TILE, wv, lane);
+        // rows q0 .. q0 + 31 < n_pad of the padded lse2 and D, or the pad run (P = 0).  The lane
+        // index is re-derived here: a choice between two captured variables would become a load
+        // through a chosen pointer and keep both in scratch memory.
+        const int ln = threadIdx.x & 63;
+        const float* src = kind < 0 ? p.ld_pad + ln
+                                    : (ln >= 32 ? p.dvec : p.lse2) + (int64_t)bh * n_pad + q0 + (ln & 31);
+        issue_dword_at(src, lds_ld + st * LDSTAGE + wv * (2 * kSub * 4), 0);
     };
-    // load instructions one issue() leaves in flight on this wavefront
-    constexpr int PER = 2 * (kSub * D / 512 / NW);
-    const int per = PER + (wv == 0 ? 1 : 0);
-    // wait until sub-chunk x (issued before the `later` sub-chunks still in flight) has landed
+    // load instructions one issue() leaves in flight on a wavefront
+    constexpr int PER = 2 * (kSub * D / 512 / NW) + 1;
+    // wait until the sub-chunk issued before `later` still-requested ones has landed
     auto wait_for = [&](int later) {
-        if (later >= 2) {
-            if (per == PER) wait_vm<2 * PER>(); else wait_vm<2 * (PER + 1)>();
-        } else if (later == 1) {
-            if (per == PER) wait_vm<PER>(); else wait_vm<PER + 1>();
-        } else {
+        if (later >= 2)
+            wait_vm<2 * PER>();
+        else if (later == 1)
+            wait_vm<PER>();
+        else
             wait_vm<0>();
-        }
     };
     static_assert(PD - 1 <= 2, "wait_for covers up to two later sub-chunks");
-    // Pair (query row r of the sub-chunk, this lane's key) takes part when lo <= r < hi: rows
-    // past n and, on the diagonal block, queries that precede the key are out; a malformed
-    // sub-chunk has hi = 0.  Both bounds are returned minus 4 hf, the lane's accumulator offset.
-    auto bounds = [&](int x, int& rlo, int& rhi) {
-        int64_t i, bh, q0;
-        locate(x, i, bh, q0);
-        const int64_t left = n - q0;
-        const int hi_ = i < 0 ? 0 : (left < kSub ? (int)left : kSub);
-        const int lo_ = (i == j) ? kloc - (int)(q0 - j * BLK) : 0;
-        rlo = lo_ - 4 * hf;
-        rhi = hi_ - 4 * hf;
+    // Masked step: pair (query row r of the sub-chunk, this lane's key) takes part when r >= rlo,
+    // i.e. on the diagonal block the query does not precede the key; returned minus 4 hf, the
+    // lane's accumulator row offset.  Rows past n and excluded entries have lse2 = +inf (P = 0).
+    auto row_lo = [&](int x) {
+        const int k = fetch(tkind, x);
+        return (k >= 0 && k < BLK) ? kloc - k - 4 * hf : -64;
     };
     const int vr_lane = 4 * hf + ((lane & 15) >> 2);
     const int vc_lane = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
     constexpr int NMF = D / 8;     // matrix-core instructions per phase (2 x D / 16)
     constexpr int EPM = 16 / NMF;  // score elements (of 16 per lane) per instruction of phase 1
     constexpr int NDB = D / 32;
     static_assert(EPM * NMF == 16 && 2 * NDB * 2 == NMF, "phase shapes");
 
-    // S = Q K^T and dP = dO V^T of the sub-chunk in stage st; instruction x: kk = x / 2,
-    // x % 2 picks S or dP
-    auto sc_frag = [&](int st, int x) { return row_fragment<D>(((x & 1) ? sO : sQ)[st], l32, 2 * (x >> 1) + hf); };
+    // LDS byte addresses of this lane's operand reads in stage 0, tile 0: the row fragments of
+    // S, dP (one per 16 columns kk) and the two transposed halves of each 32-column block db.
+    // A step adds its stage once per address and hides the sums from the compiler (empty asm),
+    // so that tiles and 16-row slices stay constant offsets in the reads' offset field rather
+    // than being re-associated into one address register per read.
+    uint32_t so[D / 16], to[2 * NDB];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) so[kk] = lds_t + 2 * Sw2<D>::off(l32, 2 * kk + hf);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) to[2 * db + h] = lds_t + 2 * Sw2<D>::toff(vr_lane + 8 * h, 32 * db + vc_lane);
+    const uint32_t ldo = lds_ld + wv * (2 * kSub * 4) + 16 * hf;
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+    // S = Q K^T and dP = dO V^T, instruction x: kk = x / 2, x % 2 picks S or dP; sb holds the
+    // stage's row-fragment addresses
+    auto sc_frag = [&](const uint32_t(&sb)[D / 16], int x) {
+        return *(lds_bf16x8*)(uintptr_t)(sb[x >> 1] + (x & 1) * TILE);
+    };
+    auto stage_bases = [](const auto& src, auto& dst, uint32_t off) {
+        constexpr int CNT = sizeof(src) / sizeof(src[0]);
+#pragma unroll
+        for (int k = 0; k < CNT; ++k) {
+            dst[k] = src[k] + off;
+            asm volatile("" : "+v"(dst[k]));
+        }
+    };
     auto sc_mfma = [&](f32x16& s, f32x16& dp, int x, bf16x8 a) {
         if (x & 1)
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[x >> 1], dp, 0, 0, 0);
@@ -162,20 +220,30 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
 
     // One step: [S, dP of sub-chunk t + 1 (stage sn)] || [P, dS of sub-chunk t (stage st)], then
-    // dV^T += dO^T P, dK^T += Q^T dS of sub-chunk t.  s, dp hold S, dP of t; sn_, dpn receive t + 1.
-    auto step = [&](auto has_next, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn, int st, int sn, int rlo,
-                    int rhi) {
+    // dV^T += dO^T P, dK^T += Q^T dS of sub-chunk t.  s, dp hold S, dP of t; sn_, dpn receive
+    // t + 1.
+    auto step = [&](auto has_next, auto masked, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn, int st, int rlo) {
         constexpr bool NEXT = decltype(has_next)::value;
+        constexpr bool MASK = decltype(masked)::value;
+        const uint32_t so_t = st * STAGE, so_n = (st + 1 < NST ? st + 1 : 0) * STAGE;
+        uint32_t lo_t = ldo + st * LDSTAGE;
+        asm volatile("" : "+v"(lo_t));
+        uint32_t sbn[D / 16], tb[2 * NDB];
+        if constexpr (NEXT) stage_bases(so, sbn, so_n);
+        stage_bases(to, tb, so_t);
+        auto ld_group = [&](int r4, int which) {  // lse2 (0) or D (1) of rows 8 r4 + 4 hf + 0..3
+            return *(lds_f32x4*)(uintptr_t)(lo_t + (which * kSub * 4 + r4 * 32));
+        };
         uint32_t pp[8], ps[8];
-        float4 gl[2], gd[2];  // log-sum-exp and D of 4 query rows, one group ahead
-        gl[0] = *(const float4*)&sLD[st][4 * hf];
-        gd[0] = *(const float4*)&sLD[st][kSub + 4 * hf];
+        f32x4 gl[2], gd[2];  // lse2 and D of 4 query rows, one group ahead
+        gl[0] = ld_group(0, 0);
+        gd[0] = ld_group(0, 1);
         bf16x8 fa[3];
         if constexpr (NEXT) {
             sn_ = f32x16{};
             dpn = f32x16{};
-            fa[0] = sc_frag(sn, 0);
-            fa[1] = sc_frag(sn, 1);
+            fa[0] = sc_frag(sbn, 0);
+            fa[1] = sc_frag(sbn, 1);
         }
         float pw[4], dsv[4];
         __builtin_amdgcn_sched_barrier(0);
@@ -183,22 +251,22 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int x = 0; x < NMF; ++x) {
             if constexpr (NEXT) {
                 sc_mfma(sn_, dpn, x, fa[x % 3]);
-                if (x + 2 < NMF) fa[(x + 2) % 3] = sc_frag(sn, x + 2);
+                if (x + 2 < NMF) fa[(x + 2) % 3] = sc_frag(sbn, x + 2);
             }
 #pragma unroll
             for (int u = 0; u < EPM; ++u) {
                 const int r = x * EPM + u;  // accumulator element: query row 8 (r / 4) + 4 hf + r % 4
                 const int r4 = r >> 2, e = r & 3;
                 if (e == 0 && r4 + 1 < 4) {
-                    gl[(r4 + 1) & 1] = *(const float4*)&sLD[st][8 * (r4 + 1) + 4 * hf];
-                    gd[(r4 + 1) & 1] = *(const float4*)&sLD[st][kSub + 8 * (r4 + 1) + 4 * hf];
+                    gl[(r4 + 1) & 1] = ld_group(r4 + 1, 0);
+                    gd[(r4 + 1) & 1] = ld_group(r4 + 1, 1);
                 }
-                const float4 lq = gl[r4 & 1], dq = gd[r4 & 1];
-                const float lv = e == 0 ? lq.x : e == 1 ? lq.y : e == 2 ? lq.z : lq.w;
-                const float dvv = e == 0 ? dq.x : e == 1 ? dq.y : e == 2 ? dq.z : dq.w;
-                const int rc = 8 * r4 + e;
-                const bool ok = rc >= rlo && rc < rhi;
-                pw[e] = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -lv * kLog2e)) : 0.f;
+                const float lv = gl[r4 & 1][e], dvv = gd[r4 & 1][e];
+                const float ex = __builtin_amdgcn_exp2f(fmaf(s[r], p.scale_log2, -lv));
+                if constexpr (MASK)
+                    pw[e] = (8 * r4 + e >= rlo) ? ex : 0.f;
+                else
+                    pw[e] = ex;
                 dsv[e] = pw[e] * (dp[r] - dvv);
                 if (e & 1) {
                     pp[2 * r4 + (e >> 1)] = pack_bf16x2(pw[e - 1], pw[e]);
@@ -209,9 +277,13 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
 
         // instruction y: y % 2 picks dV or dK, d block (y / 2) % NDB, 16-query slice y / (2 NDB)
-        auto t_frag = [&](int y) {
+        auto t_frag = [&](int y) {  // dO (y even) or Q (y odd) of stage st, transposed
             const int sl = y / (2 * NDB), db = (y >> 1) % NDB;
-            return t_fragment<D>(((y & 1) ? sQ : sO)[st], 16 * sl + vr_lane, 32 * db + vc_lane);
+            const uint32_t c = ((y & 1) ? 0 : TILE) + sl * 16 * D * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(tb[2 * db] + c));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(tb[2 * db + 1] + c));
+            const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+            return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
         };
         bf16x8 ta[3];
         ta[0] = t_frag(0);
@@ -233,7 +305,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
 
     if (NSUB > 0) {
-        // NSUB is even (two sub-chunks per unit), so at least sub-chunks 0 and 1 exist
+        // NSUB and NM are even (two sub-chunks per unit), so sub-chunks 0 and 1 exist
         for (int x = 0; x < PD && x < NSUB; ++x) issue(x, x);
         wait_for((PD < NSUB ? PD : NSUB) - 1);
         __builtin_amdgcn_s_barrier();
@@ -242,32 +314,31 @@ void bwd_dkdv_kernel(BwdParams p) {
         sA = f32x16{};
         dpA = f32x16{};
 #pragma unroll
-        for (int x = 0; x < NMF; ++x) sc_mfma(sA, dpA, x, sc_frag(0, x));
-        int rlo, rhi;
-        bounds(0, rlo, rhi);
+        for (int x = 0; x < NMF; ++x) sc_mfma(sA, dpA, x, sc_frag(so, x));
         using T_ = std::integral_constant<bool, true>;
         using F_ = std::integral_constant<bool, false>;
         // one iteration for sub-chunk t (t + 1 < NSUB): wait for t + 1, request t + PD
-        auto body = [&](int t, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn) {
-            const int in_flight_last = (t + PD - 1 < NSUB ? t + PD - 1 : NSUB - 1);  // newest requested
-            wait_for(in_flight_last - (t + 1));
+        auto body = [&](auto masked, int t, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn) {
+            const int rlo = decltype(masked)::value ? row_lo(t) : 0;
+            const int newest = (t + PD - 1 < NSUB ? t + PD - 1 : NSUB - 1);  // last requested sub-chunk
+            wait_for(newest - (t + 1));
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if (t + PD < NSUB) issue(t + PD, (t + PD) % NST);
-            int nlo, nhi;
-            bounds(t + 1, nlo, nhi);
-            step(T_{}, s, dp, sn_, dpn, t % NST, (t + 1) % NST, rlo, rhi);
-            rlo = nlo;
-            rhi = nhi;
+            step(T_{}, masked, s, dp, sn_, dpn, t % NST, rlo);
         };
         int t = 0;
-        for (; t + 2 < NSUB; t += 2) {
-            body(t, sA, dpA, sB, dpB);
-            body(t + 1, sB, dpB, sA, dpA);
+        for (; t + 2 <= NM && t + 2 < NSUB; t += 2) {  // the diagonal prefix
+            body(T_{}, t, sA, dpA, sB, dpB);
+            body(T_{}, t + 1, sB, dpB, sA, dpA);
         }
-        // NSUB even: t = NSUB - 2 here
-        body(t, sA, dpA, sB, dpB);
-        step(F_{}, sB, dpB, sA, dpA, (t + 1) % NST, 0, rlo, rhi);
+        for (; t + 2 < NSUB; t += 2) {
+            body(F_{}, t, sA, dpA, sB, dpB);
+            body(F_{}, t + 1, sB, dpB, sA, dpA);
+        }
+        // t = NSUB - 2: the last two sub-chunks, masked (correct for any sub-chunk)
+        body(T_{}, t, sA, dpA, sB, dpB);
+        step(F_{}, T_{}, sB, dpB, sA, dpA, (t + 1) % NST, row_lo(t + 1));
     }
 
     // lane holds d = 32 db + 8 j4 + 4 hf + (0..3) of key kloc
