@@ -36,7 +36,6 @@ using namespace bwd;
 
 constexpr int kSub = 32;  // queries per sub-chunk
 constexpr int NST = 4;    // LDS stages
-constexpr int PD = NST - 1;  // sub-chunks requested ahead of the one in use
 
 template <int N>
 __device__ inline void wait_vm() {
@@ -144,31 +143,54 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const uint32_t lds_t = lds_addr(&sT[0][0][0]);
     const uint32_t lds_ld = (uint32_t)(uintptr_t)(const lds_void*)&sLD[0][0];
-    auto issue = [&](int x, int st) {
+    // Copy of sub-chunk x into stage st, prepared once and issued in NLD single-instruction
+    // parts so that the copies can be spread between matrix-core instructions: the Q tile
+    // (NI_W instructions of 64 x 16 bytes per wavefront), the dO tile (NI_W) and the lse2/D run
+    // (one dword per lane).  Rows past the head's last row are clamped to it.
+    constexpr int NI_W = kSub * D / 512 / NW;
+    constexpr int NLD = 2 * NI_W + 1;  // load instructions per copy, the same on every wavefront
+    struct Copy {
+        const char* qb;
+        const char* ob;
+        const float* src;
+        int delta, lim;
+        uint32_t lds, ldl;
+    };
+    auto prepare = [&](int x, int st) {
+        Copy c;
         const int bh = fetch(tbh, x), q0 = fetch(tq0, x), kind = fetch(tkind, x);
-        const int64_t r0 = (int64_t)bh * n, last = r0 + n - 1;
-        issue_tile_at<D, NW, kSub>((const __bf16*)p.q, r0 + q0, last, lds_t + st * STAGE, wv, lane);
-        issue_tile_at<D, NW, kSub>((const __bf16*)p.d_o, r0 + q0, last, lds_t + st * STAGE + TILE, wv, lane);
+        const int64_t r0 = (int64_t)bh * n, row0 = r0 + q0, last = r0 + n - 1;
+        const int64_t bse = row0 < last ? row0 : last;
+        c.delta = (int)(row0 - bse);
+        c.lim = (int)(last - bse);
+        c.qb = (const char*)((const __bf16*)p.q + bse * D);
+        c.ob = (const char*)((const __bf16*)p.d_o + bse * D);
+        c.lds = lds_t + st * STAGE;
+        c.ldl = lds_ld + st * LDSTAGE + wv * (2 * kSub * 4);
         // rows q0 .. q0 + 31 < n_pad of the padded lse2 and D, or the pad run (P = 0).  The lane
         // index is re-derived here: a choice between two captured variables would become a load
         // through a chosen pointer and keep both in scratch memory.
         const int ln = threadIdx.x & 63;
-        const float* src = kind < 0 ? p.ld_pad + ln
-                                    : (ln >= 32 ? p.dvec : p.lse2) + (int64_t)bh * n_pad + q0 + (ln & 31);
-        issue_dword_at(src, lds_ld + st * LDSTAGE + wv * (2 * kSub * 4), 0);
+        c.src = kind < 0 ? p.ld_pad + ln : (ln >= 32 ? p.dvec : p.lse2) + (int64_t)bh * n_pad + q0 + (ln & 31);
+        return c;
     };
-    // load instructions one issue() leaves in flight on a wavefront
-    constexpr int PER = 2 * (kSub * D / 512 / NW) + 1;
-    // wait until the sub-chunk issued before `later` still-requested ones has landed
-    auto wait_for = [&](int later) {
-        if (later >= 2)
-            wait_vm<2 * PER>();
-        else if (later == 1)
-            wait_vm<PER>();
-        else
-            wait_vm<0>();
+    auto issue_part = [&](const Copy& c, int k) {
+        if (k < 2 * NI_W) {
+            const int qi = wv * NI_W + k % NI_W;
+            const int P = 64 * qi + (threadIdx.x & 63);
+            const int r = P / Sw2<D>::KCH, pc = P % Sw2<D>::KCH;
+            const int rr = (r + c.delta) < c.lim ? (r + c.delta) : c.lim;
+            copy16_to_lds(k < NI_W ? c.qb : c.ob, (uint32_t)(rr * D * 2 + ((pc ^ Sw2<D>::f(r)) << 4)),
+                          c.lds + (k < NI_W ? 0u : TILE) + 1024u * qi);
+        } else {
+            issue_dword_at(c.src, c.ldl, 0);
+        }
     };
-    static_assert(PD - 1 <= 2, "wait_for covers up to two later sub-chunks");
+    auto issue = [&](int x, int st) {
+        const Copy c = prepare(x, st);
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) issue_part(c, k);
+    };
     // Masked step: pair (query row r of the sub-chunk, this lane's key) takes part when r >= rlo,
     // i.e. on the diagonal block the query does not precede the key; returned minus 4 hf, the
     // lane's accumulator row offset.  Rows past n and excluded entries have lse2 = +inf (P = 0).
@@ -222,7 +244,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     // One step: [S, dP of sub-chunk t + 1 (stage sn)] || [P, dS of sub-chunk t (stage st)], then
     // dV^T += dO^T P, dK^T += Q^T dS of sub-chunk t.  s, dp hold S, dP of t; sn_, dpn receive
     // t + 1.
-    auto step = [&](auto has_next, auto masked, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn, int st, int rlo) {
+    constexpr int RING = 4;  // operand fragments in flight: read RING - 1 instructions ahead
+    auto step = [&](auto has_next, auto masked, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn, int st, int rlo,
+                    const Copy& cp) {
         constexpr bool NEXT = decltype(has_next)::value;
         constexpr bool MASK = decltype(masked)::value;
         const uint32_t so_t = st * STAGE, so_n = (st + 1 < NST ? st + 1 : 0) * STAGE;
@@ -238,20 +262,24 @@ void bwd_dkdv_kernel(BwdParams p) {
         f32x4 gl[2], gd[2];  // lse2 and D of 4 query rows, one group ahead
         gl[0] = ld_group(0, 0);
         gd[0] = ld_group(0, 1);
-        bf16x8 fa[3];
+        bf16x8 fa[RING];
         if constexpr (NEXT) {
             sn_ = f32x16{};
             dpn = f32x16{};
-            fa[0] = sc_frag(sbn, 0);
-            fa[1] = sc_frag(sbn, 1);
+#pragma unroll
+            for (int x = 0; x < RING - 1; ++x) fa[x] = sc_frag(sbn, x);
         }
         float pw[4], dsv[4];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < NMF; ++x) {
             if constexpr (NEXT) {
-                sc_mfma(sn_, dpn, x, fa[x % 3]);
-                if (x + 2 < NMF) fa[(x + 2) % 3] = sc_frag(sbn, x + 2);
+                sc_mfma(sn_, dpn, x, fa[x % RING]);
+                if (x + RING - 1 < NMF) fa[(x + RING - 1) % RING] = sc_frag(sbn, x + RING - 1);
+                // the copy of sub-chunk t + 3, one load instruction every few matrix-core ones
+#pragma unroll
+                for (int k = 0; k < NLD; ++k)
+                    if (x == (k * NMF) / NLD + 1) issue_part(cp, k);
             }
 #pragma unroll
             for (int u = 0; u < EPM; ++u) {
@@ -285,9 +313,9 @@ void bwd_dkdv_kernel(BwdParams p) {
             const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
             return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
         };
-        bf16x8 ta[3];
-        ta[0] = t_frag(0);
-        ta[1] = t_frag(1);
+        bf16x8 ta[RING];
+#pragma unroll
+        for (int y = 0; y < RING - 1; ++y) ta[y] = t_frag(y);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int y = 0; y < NMF; ++y) {
@@ -296,18 +324,28 @@ void bwd_dkdv_kernel(BwdParams p) {
             const bf16x8 bo = __builtin_bit_cast(
                 bf16x8, make_uint4(src[4 * sl], src[4 * sl + 1], src[4 * sl + 2], src[4 * sl + 3]));
             if (y & 1)
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[y % 3], bo, dk[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[y % RING], bo, dk[db], 0, 0, 0);
             else
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[y % 3], bo, dv[db], 0, 0, 0);
-            if (y + 2 < NMF) ta[(y + 2) % 3] = t_frag(y + 2);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[y % RING], bo, dv[db], 0, 0, 0);
+            if (y + RING - 1 < NMF) ta[(y + RING - 1) % RING] = t_frag(y + RING - 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // Pipeline over the segment's sub-chunks t (NSUB is even, so sub-chunks 0 and 1 exist):
+    //   step t: [S, dP of t + 1  ||  P, dS of t  ||  copy of t + 3], then dV, dK of t, then wait
+    //   for the copy of t + 2 and a barrier.
+    // Stage t % NST holds sub-chunk t.  The barrier ending step t makes t + 2 visible to all
+    // wavefronts and frees stage t % NST (every wavefront is done with t), which the copy of
+    // t + 4 in step t + 1 overwrites.  Copies past the last sub-chunk repeat it into a free stage,
+    // so that the number of copies in flight, and with it the wait, stays the same.
+    static_assert(NST == 4, "copies run three sub-chunks ahead");
     if (NSUB > 0) {
-        // NSUB and NM are even (two sub-chunks per unit), so sub-chunks 0 and 1 exist
-        for (int x = 0; x < PD && x < NSUB; ++x) issue(x, x);
-        wait_for((PD < NSUB ? PD : NSUB) - 1);
+        auto copy_of = [&](int x) { return prepare(x < NSUB ? x : NSUB - 1, x % NST); };
+        issue(0, 0);
+        issue(1, 1);
+        issue(NSUB > 2 ? 2 : 1, 2);
+        wait_vm<NLD>();  // sub-chunks 0 and 1 have landed
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         f32x16 sA, dpA, sB, dpB;
@@ -317,15 +355,14 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int x = 0; x < NMF; ++x) sc_mfma(sA, dpA, x, sc_frag(so, x));
         using T_ = std::integral_constant<bool, true>;
         using F_ = std::integral_constant<bool, false>;
-        // one iteration for sub-chunk t (t + 1 < NSUB): wait for t + 1, request t + PD
+        // step t with a successor (t + 1 < NSUB)
         auto body = [&](auto masked, int t, f32x16& s, f32x16& dp, f32x16& sn_, f32x16& dpn) {
             const int rlo = decltype(masked)::value ? row_lo(t) : 0;
-            const int newest = (t + PD - 1 < NSUB ? t + PD - 1 : NSUB - 1);  // last requested sub-chunk
-            wait_for(newest - (t + 1));
+            const Copy cp = copy_of(t + 3);
+            step(T_{}, masked, s, dp, sn_, dpn, t % NST, rlo, cp);
+            wait_vm<NLD>();  // the copy of t + 2 has landed (t + 3 may be in flight)
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (t + PD < NSUB) issue(t + PD, (t + PD) % NST);
-            step(T_{}, masked, s, dp, sn_, dpn, t % NST, rlo);
         };
         int t = 0;
         for (; t + 2 <= NM && t + 2 < NSUB; t += 2) {  // the diagonal prefix
@@ -338,7 +375,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
         // t = NSUB - 2: the last two sub-chunks, masked (correct for any sub-chunk)
         body(T_{}, t, sA, dpA, sB, dpB);
-        step(F_{}, T_{}, sB, dpB, sA, dpA, (t + 1) % NST, row_lo(t + 1));
+        step(F_{}, T_{}, sB, dpB, sA, dpA, (t + 1) % NST, row_lo(t + 1), Copy{});
     }
 
     // lane holds d = 32 db + 8 j4 + 4 hf + (0..3) of key kloc
