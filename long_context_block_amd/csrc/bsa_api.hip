@@ -228,7 +228,7 @@ size_t bsa_backward_workspace_bytes(int32_t batch, int32_t heads_q, int32_t head
     const int64_t nqb = (n + block - 1) / block;
     const int64_t segs = bsa::bwd_segments_upper_bound(nqb, nnz, heads_q, heads_kv, block);
     return align256((size_t)2 * batch * heads_q * nqb * block * sizeof(float)) + 256 +
-           align256((size_t)(nqb + 1) * sizeof(int32_t)) +
+           align256((size_t)(nqb + 1) * sizeof(int32_t)) + align256((size_t)segs * 4 * sizeof(int32_t)) +
            (size_t)batch * heads_kv * segs * 2 * block * d * sizeof(float);
 }
 
@@ -269,6 +269,8 @@ bsa_status bsa_backward(const void* q, const void* k, const void* v, const void*
     ws += 256;
     p.seg_ptr = (int32_t*)ws;
     ws += align256((size_t)(nqb + 1) * sizeof(int32_t));
+    p.seg_info = (int32_t*)ws;
+    ws += align256((size_t)segs * 4 * sizeof(int32_t));
     p.part = (float*)ws;
     p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv;
     p.nqb = (int32_t)nqb; p.n = n; p.n_pad = n_pad; p.nnz = nnz; p.nseg_ub = segs;

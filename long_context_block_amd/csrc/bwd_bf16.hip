@@ -221,7 +221,10 @@ __global__ __launch_bounds__(1024) void bwd_seg_kernel(BwdParams p, int cpb) {
     int64_t run = part[t] - local;
     for (int64_t j = r0; j < r1; ++j) {
         p.seg_ptr[j] = (int32_t)run;
-        run += segs(j);
+        const int64_t sj = segs(j);
+        for (int64_t s = 0; s < sj && run + s < p.nseg_ub; ++s)
+            *(int4*)(p.seg_info + 4 * (run + s)) = make_int4((int)j, (int)s, (int)sj, 0);
+        run += sj;
     }
     if (t == 1023) p.seg_ptr[nqb] = (int32_t)part[1023];
 }

@@ -59,15 +59,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int sw = (int)(blockIdx.x % p.nseg_ub);
     const int64_t nqb = p.nqb;
     if (sw >= p.seg_ptr[nqb]) return;
-    // key block j: seg_ptr[j] <= sw < seg_ptr[j + 1]
-    int64_t lo = 0, hi = nqb - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (p.seg_ptr[mid] <= sw) lo = mid; else hi = mid - 1;
-    }
-    const int j = (int)lo;
-    const int seg = sw - p.seg_ptr[j];
-    const int nseg = p.seg_ptr[j + 1] - p.seg_ptr[j];
+    // key block j of this segment, its index within the block and the block's segment count
+    const int4 info = *(const int4*)(p.seg_info + 4 * (int64_t)sw);
+    const int j = info.x, seg = info.y, nseg = info.z;
     const int64_t b = bg / p.heads_kv, g = bg % p.heads_kv;
     const int G = p.heads_q / p.heads_kv;
     const int64_t n = p.n, n_pad = p.n_pad;
@@ -77,8 +71,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     t1 = t1 < t0 ? t0 : (t1 > p.nnz ? p.nnz : t1);
     const int upt = G * UPB;  // units per entry of the transposed row
     const int units_all = (int)(t1 - t0) * upt;
-    const int u_begin = seg * kSeg;
-    const int u_end = (u_begin + kSeg < units_all) ? u_begin + kSeg : units_all;
+    // the block's units dealt evenly over its nseg = ceil(units / kSeg) segments (<= kSeg each)
+    int per_seg = nseg > 0 ? (units_all + nseg - 1) / nseg : 0;
+    per_seg = per_seg < kSeg ? per_seg : kSeg;
+    const int u_begin = seg * per_seg;
+    const int u_end = (u_begin + per_seg < units_all) ? u_begin + per_seg : units_all;
     const int NSUB = u_end > u_begin ? 2 * (u_end - u_begin) : 0;
 
     // Sub-chunk table: lane x describes sub-chunks x (index 0) and 64 + x (index 1) by batch *

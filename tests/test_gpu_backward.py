@@ -135,3 +135,36 @@ def test_backward_errors():
     with pytest.raises(bsa.BsaError) as e:
         bsa.bsa_backward(qb, qb, qb, qb, qb, lse, qb.clone(), qb.clone(), qb.clone(), rp, ci, trp, tci, 64, small)
     assert e.value.status == bsa.BSA_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("wname,n", [("qwen3_32k", 1000), ("bf1_4k", 777)])
+def test_backward_transposed_rows_in_any_order(wname, n):
+    # The dK/dV pass masks only a leading run of diagonal-block work when the transposed rows are
+    # sorted (as bsa_build_route_transpose writes them); given the same readers in reverse order it
+    # must fall back to masking every step of the affected segments and still match the oracle.
+    w = synth.WORKLOADS[wname].resized(n=n, heads_q=2, heads_kv=2 if wname == "bf1_4k" else 1)
+    q, k, v = synth.make_qkv(w)
+    g = torch.Generator("cpu").manual_seed(62)
+    d_o = torch.randn(q.shape, generator=g).to(q.dtype)
+    rp, ci = bsa.build_route(bsa.route_spec(w.route_kind, w.n_local, w.keep_first, w.n_random, w.route_seed), w.n, w.block)
+    trp, tci = bsa.build_route_transpose(rp, ci)
+    trp_h, tci_h = trp.cpu().numpy(), tci.cpu().numpy().copy()
+    for j in range(len(trp_h) - 1):
+        tci_h[trp_h[j]:trp_h[j + 1]] = tci_h[trp_h[j]:trp_h[j + 1]][::-1].copy()
+    tci_rev = torch.from_numpy(tci_h).cuda()
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), d_o.cuda()
+    o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, with_lse=True)
+    grads = []
+    for t_ci in (tci, tci_rev):
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws = torch.empty(bsa.bsa_backward_workspace_bytes(w.batch, w.heads_q, w.heads_kv, w.n, w.d, w.block, ci.numel()),
+                         dtype=torch.uint8, device="cuda")
+        bsa.bsa_backward(qd, kd, vd, o, dod, lse, dq, dk, dv, rp, ci, trp, t_ci, w.block, ws)
+        grads.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    ref = A.attention_backward(q, k, v, d_o, w.block, rp.cpu().numpy(), ci.cpu().numpy())
+    for name, got, r in zip(("dq", "dk", "dv"), grads[1], ref):
+        rl2, mx = grad_errors(got, r)
+        print(f"  reversed rows {name}: rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)
+        assert rl2 <= RELL2 and mx <= MAXREL, (name, rl2, mx)
+    assert torch.equal(grads[0][0], grads[1][0])  # dQ walks the forward route: unaffected
