@@ -10,6 +10,9 @@ path computes, written in numpy float64 from the source pages:
 * ``attn``    — block-sparse attention as masked dense softmax attention:
   the route is expanded to an explicit token mask which is applied before the
   softmax, so excluded pairs get weight exactly zero.
+* ``bsbr``    — the BSBR between-chunk retrieval term (chunk states K^T V,
+  meta attention over strictly earlier chunks, read-out by each token's
+  query), added to the within-chunk (block-diagonal) attention.
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product path (the C-ABI library and
@@ -19,9 +22,10 @@ share only the seeded input generators in ``synth.py`` (which hold none of the
 method's arithmetic).
 
 Pins (what ties this oracle to something other than itself) live in
-``tests/test_oracle_routes.py`` and ``tests/test_oracle_attn.py``; each function
+``tests/test_oracle_routes.py``, ``tests/test_oracle_attn.py`` and
+``tests/test_oracle_bsbr.py``; each function
 below names the passage it follows.  Functions with no pin say "parity
 unpinned" in their docstring.
 """
 
-from . import routes, attn  # noqa: F401
+from . import routes, attn, bsbr  # noqa: F401
