@@ -227,6 +227,34 @@ bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, v
 size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d);
 
 /*
+ * bsa_bsbr_forward — BSBR attention ("bsbr", Solution: the combined formula), chunks of
+ * `chunk` tokens, nch = ceil(n / chunk):
+ *
+ *     O[t] = softmax-attention of t over the earlier tokens of its own chunk (causal)
+ *          + Q[t]^T A_c(t),   A_c = sum over c' < c of W[c, c'] F_c',
+ *     F_c = K_c^T V_c (d x d, the chunk's tokens),  W[c, :] = softmax over c' < c of
+ *     scale * R_c . H_c'  (chunk 0 retrieves nothing).
+ *
+ * The within-chunk term is bsa_forward over the block-diagonal route (built in the workspace).
+ * Inputs (device, caller-owned, contiguous, 16-byte aligned, bf16): q [batch, heads_q, n, d];
+ * k, v [batch, heads_kv, n, d]; r_meta (meta queries) [batch, heads_q, nch, d]; h_meta (meta
+ * keys) [batch, heads_kv, nch, d].  Output o like q.  scale <= 0 selects 1/sqrt(d) for both
+ * softmaxes.  workspace: at least bsa_bsbr_workspace_bytes(...) bytes (the route, fp32 chunk
+ * states, meta weights and retrieved states); contents on entry do not matter.  Supported: BF16;
+ * d in {64, 128}; chunk in {64, 128}; 1 <= nch <= 1024.  Six kernels on `stream`, no atomics.
+ * Errors: BSA_ERR_INVALID_ARGUMENT (NULL or misaligned pointers, bad sizes), BSA_ERR_UNSUPPORTED
+ * (dtype, d, chunk, nch), BSA_ERR_CAPACITY (workspace), BSA_ERR_DEVICE (launch failure).
+ */
+bsa_status bsa_bsbr_forward(const void* q, const void* k, const void* v, const void* r_meta,
+                            const void* h_meta, void* o, int32_t batch, int32_t heads_q,
+                            int32_t heads_kv, int64_t n, int32_t d, int32_t chunk, bsa_dtype dtype,
+                            float scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes bsa_bsbr_forward needs (0 on bad input). */
+size_t bsa_bsbr_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                                int32_t chunk);
+
+/*
  * bsa_check_route — validate a CSR route held in HOST memory: row_ptr[0] == 0, row_ptr
  * non-decreasing, row_ptr[nqb] == nnz, and every row strictly ascending within [0, i] and
  * ending with i (the self block is mandatory, so no row is empty).  BSA_OK or

@@ -34,7 +34,8 @@ BSA_ROUTE_SLIDING_WINDOW = 4
 
 EXPORTS = ("bsa_build_route", "bsa_forward", "bsa_dense_causal_ref", "bsa_dense_route_workspace_bytes",
            "bsa_decode", "bsa_decode_workspace_bytes", "bsa_build_route_transpose", "bsa_backward",
-           "bsa_backward_workspace_bytes", "bsa_check_route", "bsa_status_string", "bsa_last_error")
+           "bsa_backward_workspace_bytes", "bsa_bsbr_forward", "bsa_bsbr_workspace_bytes", "bsa_check_route",
+           "bsa_status_string", "bsa_last_error")
 
 
 class BsaError(RuntimeError):
@@ -85,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.bsa_backward.restype = ctypes.c_int
         L.bsa_backward_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i64]
         L.bsa_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.bsa_bsbr_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, ctypes.c_int, f32,
+                                       vp, ctypes.c_size_t, vp]
+        L.bsa_bsbr_forward.restype = ctypes.c_int
+        L.bsa_bsbr_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32]
+        L.bsa_bsbr_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_check_route.argtypes = [vp, vp, i64, i64]
         L.bsa_check_route.restype = ctypes.c_int
         L.bsa_status_string.argtypes = [ctypes.c_int]
@@ -295,6 +301,38 @@ def backward(q, k, v, o, d_o, lse, row_ptr, col_idx, block: int, t_route=None, s
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
     bsa_backward(q, k, v, o, d_o, lse, dq, dk, dv, row_ptr, col_idx, t_row_ptr, t_col_idx, block, ws, scale, stream)
     return dq, dk, dv
+
+
+def bsa_bsbr_workspace_bytes(batch: int, heads_q: int, heads_kv: int, n: int, d: int, chunk: int) -> int:
+    return int(lib().bsa_bsbr_workspace_bytes(batch, heads_q, heads_kv, n, d, chunk))
+
+
+def bsa_bsbr_forward(q, k, v, r_meta, h_meta, o, chunk: int, workspace, scale: float = 0.0, stream=None) -> None:
+    """o = within-chunk attention + the BSBR retrieval over earlier chunks (see include/bsa.h)."""
+    dt = _dtype_code(q)
+    b, hq, n, d = q.shape
+    hkv = k.shape[1]
+    nch = -(-n // chunk)
+    for x, nm, shp in ((k, "k", (b, hkv, n, d)), (v, "v", (b, hkv, n, d)), (o, "o", (b, hq, n, d)),
+                       (r_meta, "r_meta", (b, hq, nch, d)), (h_meta, "h_meta", (b, hkv, nch, d))):
+        if tuple(x.shape) != shp:
+            raise ValueError(f"{nm} must have shape {shp}")
+    ptrs = [_dev_ptr(x, nm, q.dtype) for x, nm in ((q, "q"), (k, "k"), (v, "v"), (r_meta, "r_meta"),
+                                                      (h_meta, "h_meta"), (o, "o"))]
+    wp = _dev_ptr(workspace, "workspace")
+    _check(lib().bsa_bsbr_forward(*ptrs, b, hq, hkv, n, d, chunk, dt, float(scale), wp,
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def bsbr_forward(q, k, v, r_meta, h_meta, chunk: int, scale: float = 0.0, stream=None):
+    """Allocate the output and workspace and run bsa_bsbr_forward."""
+    import torch
+    b, hq, n, d = q.shape
+    o = torch.empty_like(q)
+    nbytes = bsa_bsbr_workspace_bytes(b, hq, k.shape[1], n, d, chunk)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    bsa_bsbr_forward(q, k, v, r_meta, h_meta, o, chunk, ws, scale, stream)
+    return o
 
 
 def bsa_check_route(row_ptr, col_idx) -> None:

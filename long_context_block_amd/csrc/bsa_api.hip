@@ -349,6 +349,70 @@ size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block) {
     return (size_t)(nqb + 1 + nqb * (nqb + 1) / 2) * sizeof(int32_t);
 }
 
+size_t bsa_bsbr_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                                int32_t chunk) {
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || n < 1 || d < 1 || chunk < 1) return 0;
+    const size_t nch = (size_t)((n + chunk - 1) / chunk);
+    return align256((2 * nch + 1) * sizeof(int32_t)) + align256((size_t)batch * heads_kv * nch * d * d * sizeof(float)) +
+           align256((size_t)batch * heads_q * nch * nch * sizeof(float)) +
+           (size_t)batch * heads_q * nch * d * d * sizeof(float);
+}
+
+bsa_status bsa_bsbr_forward(const void* q, const void* k, const void* v, const void* r_meta, const void* h_meta,
+                            void* o, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
+                            int32_t chunk, bsa_dtype dtype, float scale, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    if (batch < 0 || heads_q < 1 || heads_kv < 1 || n < 0 || d < 1 || chunk < 1)
+        return fail(BSA_ERR_INVALID_ARGUMENT,
+                    "sizes must satisfy batch >= 0, heads >= 1, n >= 0, d >= 1, chunk >= 1 "
+                    "(got batch=%d heads_q=%d heads_kv=%d n=%lld d=%d chunk=%d)",
+                    batch, heads_q, heads_kv, (long long)n, d, chunk);
+    if (heads_q % heads_kv != 0)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+    if (dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "BSBR supports bf16 only");
+    if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim d=%d not supported (64 or 128)", d);
+    if (chunk != 64 && chunk != 128) return fail(BSA_ERR_UNSUPPORTED, "chunk=%d not supported (64 or 128)", chunk);
+    if (!(scale <= 0.f) && !std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    const int64_t nch = (n + chunk - 1) / chunk;
+    if (nch > 1024) return fail(BSA_ERR_UNSUPPORTED, "%lld chunks exceed 1024", (long long)nch);
+    if (batch == 0 || n == 0) return ok();
+    if (!q || !k || !v || !r_meta || !h_meta || !o || !workspace)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, r_meta, h_meta, o and workspace must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(r_meta) || !aligned16(h_meta) || !aligned16(o) ||
+        !aligned16(workspace))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "all tensors and the workspace must be 16-byte aligned");
+    const size_t need = bsa_bsbr_workspace_bytes(batch, heads_q, heads_kv, n, d, chunk);
+    if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
+    if ((int64_t)batch * heads_q * nch > INT32_MAX || (int64_t)batch * heads_q * nch * d * d / 1024 > INT32_MAX)
+        return fail(BSA_ERR_UNSUPPORTED, "grid too large");
+    // the within-chunk term: the forward over the block-diagonal route, built into the workspace
+    char* ws = (char*)workspace;
+    int32_t* rp = (int32_t*)ws;
+    int32_t* ci = rp + nch + 1;
+    ws += align256((size_t)(2 * nch + 1) * sizeof(int32_t));
+    bsa_route_spec spec;
+    memset(&spec, 0, sizeof(spec));
+    spec.kind = BSA_ROUTE_BLOCK_DIAGONAL;
+    hipError_t e = bsa::launch_route_build(spec, nch, rp, ci, stream);
+    if (e != hipSuccess) return device_error(e, "BSBR route build launch");
+    bsa_status s = run_forward(q, k, v, o, nullptr, batch, heads_q, heads_kv, n, d, chunk, dtype, scale, rp, ci, nch,
+                               stream);
+    if (s != BSA_OK) return s;
+    bsa::BsbrParams p;
+    p.q = q; p.k = k; p.v = v; p.r = r_meta; p.h = h_meta; p.o = o;
+    p.F = (float*)ws;
+    ws += align256((size_t)batch * heads_kv * nch * d * d * sizeof(float));
+    p.W = (float*)ws;
+    ws += align256((size_t)batch * heads_q * nch * nch * sizeof(float));
+    p.A = (float*)ws;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.nch = (int32_t)nch; p.n = n;
+    const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
+    p.scale_log2 = (float)(sc * 1.4426950408889634073599);
+    e = bsa::launch_bsbr_retrieval(p, d, chunk, stream);
+    if (e != hipSuccess) return device_error(e, "BSBR retrieval launch");
+    return ok();
+}
+
 bsa_status bsa_dense_causal_ref(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
                                 int32_t block, bsa_dtype dtype, float scale, int32_t* route_workspace,

@@ -74,29 +74,30 @@ def meta_weights(r, h, heads_q: int, scale: float) -> np.ndarray:
     return W
 
 
-def retrieval(q, k, v, r, h, B: int, scale: float | None = None) -> np.ndarray:
-    """The between-chunk term out[b, h_q, t] = Q[t]^T A_c(t) (fp64, shape of q)."""
+def retrieval(q, k, v, r, h, B: int, scale: float | None = None, rows=None) -> np.ndarray:
+    """The between-chunk term out[b, h_q, t] = Q[t]^T A_c(t) (fp64, [b, h_q, len(rows), d];
+    rows defaults to every token)."""
     qq = _to_f64(q)
     b, hq, n, d = qq.shape
     hkv = _to_f64(k).shape[1]
     G = hq // hkv
     sc = 1.0 / math.sqrt(d) if scale is None or scale <= 0 else float(scale)
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
     F = chunk_states(k, v, B)
     W = meta_weights(r, h, hq, sc)
-    out = np.zeros_like(qq)
-    nch = F.shape[2]
+    out = np.zeros((b, hq, len(rows), d))
     for hd in range(hq):
-        A = np.einsum("bce,beij->bcij", W[:, hd], F[:, hd // G])  # [b, nch, d, d]
-        for c in range(nch):
-            s0, s1 = c * B, min(n, (c + 1) * B)
-            out[:, hd, s0:s1] = np.einsum("bti,bij->btj", qq[:, hd, s0:s1], A[:, c])
+        for c in np.unique(rows // B):
+            A = np.einsum("be,beij->bij", W[:, hd, c], F[:, hd // G])  # retrieved state of chunk c
+            sel = np.nonzero(rows // B == c)[0]
+            out[:, hd, sel] = np.einsum("bti,bij->btj", qq[:, hd, rows[sel]], A)
     return out
 
 
-def bsbr_forward(q, k, v, r, h, B: int, scale: float | None = None) -> np.ndarray:
+def bsbr_forward(q, k, v, r, h, B: int, scale: float | None = None, rows=None) -> np.ndarray:
     """O = retrieval term + within-chunk causal attention (the block-diagonal route)."""
     from . import attn, routes
     n = _to_f64(q).shape[2]
     rp, ci = routes.route_csr(routes.BLOCK_DIAGONAL, n, B)
-    within = attn.attention(q, k, v, B, rp, ci, scale=scale)
-    return within + retrieval(q, k, v, r, h, B, scale=scale)
+    within = attn.attention(q, k, v, B, rp, ci, scale=scale, rows=rows)
+    return within + retrieval(q, k, v, r, h, B, scale=scale, rows=rows)

@@ -93,3 +93,15 @@ def make_qkv(w: Workload, seed: int | None = None):
     v = torch.randn(w.batch, w.heads_kv, w.n, w.d, generator=g, dtype=torch.float32)
     dt = w.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)
+
+
+def make_meta(w: Workload, seed: int | None = None):
+    """Seeded host tensors (r, h) for the BSBR retrieval term: one meta query per chunk and query
+    head, one meta key per chunk and key/value head, N(0, 1) in the workload's dtype (chunk width =
+    the workload's block)."""
+    g = torch.Generator("cpu").manual_seed((w.input_seed if seed is None else seed) + 1000)
+    nch = -(-w.n // w.block)
+    r = torch.randn(w.batch, w.heads_q, nch, w.d, generator=g, dtype=torch.float32)
+    h = torch.randn(w.batch, w.heads_kv, nch, w.d, generator=g, dtype=torch.float32)
+    dt = w.torch_dtype
+    return r.to(dt), h.to(dt)

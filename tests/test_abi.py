@@ -121,6 +121,47 @@ def test_dense_ref_rejects_small_workspace():
     assert st == bsa.BSA_ERR_INVALID_ARGUMENT
 
 
+def _raw_bsbr(**kw):
+    args = dict(q=16, k=16, v=16, r=16, h=16, o=16, batch=1, hq=2, hkv=1, n=1000, d=64, chunk=128, dtype=0,
+                scale=0.0, ws=16, wsb=None, stream=None)
+    args.update(kw)
+    if args["wsb"] is None:
+        args["wsb"] = bsa.bsa_bsbr_workspace_bytes(max(args["batch"], 0), args["hq"], max(args["hkv"], 1),
+                                                   max(args["n"], 1), args["d"], max(args["chunk"], 1))
+    return bsa.lib().bsa_bsbr_forward(args["q"], args["k"], args["v"], args["r"], args["h"], args["o"],
+                                      args["batch"], args["hq"], args["hkv"], args["n"], args["d"], args["chunk"],
+                                      args["dtype"], args["scale"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(chunk=0), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=1), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(d=96), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(chunk=32), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(n=128 * 1024 + 1), bsa.BSA_ERR_UNSUPPORTED),
+    (dict(r=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(h=24), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (dict(wsb=100), bsa.BSA_ERR_CAPACITY),
+    (dict(scale=float("inf")), bsa.BSA_ERR_INVALID_ARGUMENT),
+])
+def test_bsbr_rejects_bad_arguments(kw, status):
+    assert _raw_bsbr(**kw) == status
+    assert bsa.bsa_last_error() != ""
+
+
+def test_bsbr_workspace_and_empty_batch():
+    # route (2 nch + 1 ints), fp32 states per kv head, meta weights and retrieved states per query head
+    nch, d, hq, hkv = 8, 64, 3, 1
+    align = lambda x: -(-x // 256) * 256  # noqa: E731
+    want = align((2 * nch + 1) * 4) + align(hkv * nch * d * d * 4) + align(hq * nch * nch * 4) + hq * nch * d * d * 4
+    assert bsa.bsa_bsbr_workspace_bytes(1, 3, 1, 1000, 64, 128) == want
+    assert bsa.bsa_bsbr_workspace_bytes(1, 3, 2, 1000, 64, 128) == 0
+    assert _raw_bsbr(batch=0, q=None, k=None, v=None, r=None, h=None, o=None, ws=None) == bsa.BSA_OK
+
+
 ROUTE_CASES = [
     (R.BF1, dict(n_local=2, keep_first=1)), (R.BF1, dict(n_local=1, keep_first=1)),
     (R.BF1, dict(n_local=0, keep_first=0)), (R.BF1, dict(n_local=5, keep_first=1)),

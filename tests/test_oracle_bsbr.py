@@ -155,3 +155,10 @@ def test_two_earlier_chunks_weigh_by_the_logistic_of_the_scaled_score_gap():
     F = OB.chunk_states(k, v, 4)
     want = q[0, 0, 9] @ (W[0, 0, 2, 0] * F[0, 0, 0] + W[0, 0, 2, 1] * F[0, 0, 1])
     assert np.allclose(out[0, 0, 9], want, rtol=1e-13, atol=1e-13)
+
+
+def test_row_subsets_equal_the_full_result():
+    q, k, v, r, h = rng_inputs(12, hq=2, hkv=1, n=23, d=3, B=4)
+    full = OB.bsbr_forward(q, k, v, r, h, 4)
+    rows = np.array([0, 3, 4, 9, 22])
+    assert np.allclose(OB.bsbr_forward(q, k, v, r, h, 4, rows=rows), full[:, :, rows], rtol=1e-13, atol=1e-13)
