@@ -18,12 +18,13 @@
 //    (i / 32, j / 32) sits at [(tile * 32 + j % 32) * 32 + i % 32], tile = (i / 32) * d / 32 + j / 32.
 //  * bsbr_meta_kernel: one wavefront per (batch, query head, chunk): dot products of R_c with the
 //    earlier H rows, max and sum across the wavefront, and the full row of W (zeros at c' >= c).
-//  * bsbr_mix_kernel: A = W F as a small GEMM per (batch, query head) over the flattened d*d
-//    states (layout-agnostic): a work-group takes 16 chunks x 1024 state elements; the 16 rows of
-//    W are staged in LDS transposed, so each earlier chunk's state slice is read once per group.
-//  * bsbr_apply_kernel: one work-group per (batch, query head, chunk >= 1): A_c is staged in LDS
-//    row-major, each thread holds one token's query (fp32) and adds Q[t]^T A_c to a slice of the
-//    output row, which it reads, adds to and rounds to bf16 once more.
+//  * bsbr_mix_kernel: A = W F as a small fp32 GEMM per (batch, query head) over the flattened
+//    d*d states (layout-agnostic): a work-group takes 16 chunks x 64 state elements, its four
+//    wavefronts split the earlier chunks and their partials are summed in LDS in a fixed order;
+//    W is stored transposed, so the group's weights are staged in LDS with one coalesced pass.
+//  * bsbr_apply_kernel: one work-group per (batch, query head, chunk >= 1), one wavefront per 32
+//    tokens: O^T += A_c^T Q^T on the matrix cores with A_c split into two bf16 parts (hi, lo),
+//    then read, add and round the bf16 output once more.
 
 #include "bwd_common.hpp"
 
@@ -42,6 +43,11 @@ __global__ __launch_bounds__(256) void bsbr_state_kernel(BsbrParams p) {
     const int64_t bg = w / p.nch;
     const int64_t n = p.n, t0 = (int64_t)c * BLK;
     const int rows = (int)((n - t0) < BLK ? (n - t0) : BLK);
+    if (bg == 0 && threadIdx.x == 0) {  // the block-diagonal route of the within-chunk term
+        p.route_rp[c] = c;
+        p.route_ci[c] = c;
+        if (c == p.nch - 1) p.route_rp[c + 1] = c + 1;
+    }
     const __bf16* K = (const __bf16*)p.k + (bg * n + t0) * D;
     const __bf16* V = (const __bf16*)p.v + (bg * n + t0) * D;
     constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -125,15 +131,25 @@ __global__ __launch_bounds__(64) void bsbr_meta_kernel(BsbrParams p) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
     const float inv = c > 0 ? 1.f / sum : 0.f;
-    float* Wr = p.W + w * nch;
-    for (int cp = lane; cp < nch; cp += 64) Wr[cp] = cp < c ? __builtin_amdgcn_exp2f(score(cp) - mx) * inv : 0.f;
+    // stored transposed, W^T[c'][c], so that the mix reads the weights of consecutive chunks c
+    // for one earlier chunk c' as one scalar load
+    float* Wt = p.W + bh * nch * (int64_t)nch + c;
+    for (int cp = lane; cp < nch; cp += 64)
+        Wt[(int64_t)cp * nch] = cp < c ? __builtin_amdgcn_exp2f(score(cp) - mx) * inv : 0.f;
 }
 
-constexpr int kMixRows = 16;     // chunks per mix work-group
-constexpr int kMixCols = 1024;   // state elements per mix work-group (4 per thread)
+constexpr int kMixRows = 16;   // chunks per work-group (accumulators per thread)
+constexpr int kMixCols = 64;   // state elements per work-group (one per lane)
+constexpr int kMixPf = 8;      // earlier chunks per wavefront step (their loads issued together)
 
+// A[c][e] = sum over c' < c of W[c][c'] F[c'][e].  Work-group = 16 chunks c x 64 state elements e;
+// its 4 wavefronts split the earlier chunks c' (wavefront w takes c' = w mod 4) so that each
+// lane's chain of dependent loads is a quarter as long, and sum their partials in LDS in a fixed
+// order.  The group's weights (16 per earlier chunk, contiguous in W^T) are staged in LDS once
+// and read back as broadcasts.
 __global__ __launch_bounds__(256) void bsbr_mix_kernel(BsbrParams p, int dd) {
-    extern __shared__ __attribute__((aligned(16))) float sW[];  // [c'][16]: W of the group's 16 chunks, transposed
+    __shared__ float part[4][kMixRows][kMixCols];
+    extern __shared__ __attribute__((aligned(16))) float sWt[];  // [c' < cmax][16]
     const int nch = p.nch;
     const int slices = dd / kMixCols;
     const int groups = (nch + kMixRows - 1) / kMixRows;
@@ -143,130 +159,146 @@ __global__ __launch_bounds__(256) void bsbr_mix_kernel(BsbrParams p, int dd) {
     const int64_t bh = w / slices / groups;
     const int64_t b = bh / p.heads_q, h = bh % p.heads_q;
     const int G = p.heads_q / p.heads_kv;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c0 = grp * kMixRows;
     const int rows = (nch - c0) < kMixRows ? nch - c0 : kMixRows;
-    const int cmax = c0 + rows - 1;  // earlier chunks of the group's last chunk: c' < cmax
-    for (int x = threadIdx.x; x < kMixRows * cmax; x += 256) {
-        const int u = x / cmax, cp = x % cmax;
-        sW[cp * kMixRows + u] = u < rows ? p.W[(bh * nch + c0 + u) * nch + cp] : 0.f;
-    }
-    __syncthreads();
-    const int e = slice * kMixCols + 4 * threadIdx.x;
+    const int cmax = c0 + rows - 1;  // the group's last chunk reads chunks c' < cmax
+    const int e = slice * kMixCols + lane;
     const float* Fg = p.F + (b * p.heads_kv + h / G) * (int64_t)nch * dd + e;
-    float4 acc[kMixRows];
+    // W^T row c' for this group: Wt[c' * nch + c0 .. + 16].  All 16 are read even when the group
+    // has fewer chunks (the workspace pads W by 16 floats); the extra rows are never stored.
+    const float* Wt = p.W + bh * nch * (int64_t)nch + c0;
+    for (int x = threadIdx.x; x < cmax * kMixRows; x += 256)
+        sWt[x] = Wt[(int64_t)(x / kMixRows) * nch + x % kMixRows];
+    __syncthreads();
+    float acc[kMixRows];
 #pragma unroll
-    for (int u = 0; u < kMixRows; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int cp = 0; cp < cmax; ++cp) {
-        const float4 f = *(const float4*)(Fg + (int64_t)cp * dd);
-        const float4* wr = (const float4*)(sW + cp * kMixRows);
+    for (int u = 0; u < kMixRows; ++u) acc[u] = 0.f;
+    for (int cb = wv; cb < cmax; cb += 4 * kMixPf) {
+        float f[kMixPf];
 #pragma unroll
-        for (int q4 = 0; q4 < kMixRows / 4; ++q4) {
-            const float4 wq = wr[q4];
-            const float ws[4] = {wq.x, wq.y, wq.z, wq.w};
+        for (int y = 0; y < kMixPf; ++y) {
+            const int cp = cb + 4 * y;
+            f[y] = cp < cmax ? Fg[(int64_t)cp * dd] : 0.f;
+        }
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                float4& a = acc[4 * q4 + y];
-                a.x = fmaf(ws[y], f.x, a.x);
-                a.y = fmaf(ws[y], f.y, a.y);
-                a.z = fmaf(ws[y], f.z, a.z);
-                a.w = fmaf(ws[y], f.w, a.w);
+        for (int y = 0; y < kMixPf; ++y) {
+            const int cp = cb + 4 * y;
+            if (cp >= cmax) break;
+            const float4* wr = (const float4*)(sWt + cp * kMixRows);
+#pragma unroll
+            for (int q4 = 0; q4 < kMixRows / 4; ++q4) {
+                const float4 wq = wr[q4];
+                acc[4 * q4] = fmaf(wq.x, f[y], acc[4 * q4]);
+                acc[4 * q4 + 1] = fmaf(wq.y, f[y], acc[4 * q4 + 1]);
+                acc[4 * q4 + 2] = fmaf(wq.z, f[y], acc[4 * q4 + 2]);
+                acc[4 * q4 + 3] = fmaf(wq.w, f[y], acc[4 * q4 + 3]);
             }
         }
     }
 #pragma unroll
-    for (int u = 0; u < kMixRows; ++u)
-        if (u < rows) *(float4*)(p.A + (bh * nch + c0 + u) * (int64_t)dd + e) = acc[u];
+    for (int u = 0; u < kMixRows; ++u) part[wv][u][lane] = acc[u];
+    __syncthreads();
+    // wavefront w sums rows u = 4 w .. 4 w + 3 over the four partials, in order
+    float* Ao = p.A + (bh * nch + c0) * (int64_t)dd + e;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+        const int u = 4 * wv + y;
+        if (u < rows) Ao[(int64_t)u * dd] = ((part[0][u][lane] + part[1][u][lane]) + part[2][u][lane]) + part[3][u][lane];
+    }
 }
 
+// O^T[j][t] += sum_i A_c[i][j] Q[t][i] on the matrix cores: A operand = A_c^T (32 columns j x 16
+// rows i, contiguous in the state's tile layout), B operand = Q^T (16 i x 32 tokens, contiguous in
+// Q's rows).  A_c is fp32; it is split into hi = bf16(A) and lo = bf16(A - hi), both multiplied
+// by the (exact) bf16 Q, so the product keeps ~16 significant bits of A.  One wavefront per 32
+// tokens; the accumulator gives each lane one token and 4 consecutive columns per register group.
 template <int D, int BLK>
-__global__ __launch_bounds__(256) void bsbr_apply_kernel(BsbrParams p) {
-    __shared__ __attribute__((aligned(16))) float sA[D * D];  // A_c row-major [i][j]
+__global__ __launch_bounds__(BLK / 32 * 64) void bsbr_apply_kernel(BsbrParams p) {
+    __shared__ __attribute__((aligned(16))) float sA[D * D];  // A_c in the tile layout
     const int nch = p.nch;
     const int64_t w = blockIdx.x;  // (b * heads_q + h) * nch + c
     const int c = (int)(w % nch);
     if (c == 0) return;            // chunk 0 retrieves nothing
     const int64_t bh = w / nch;
-    const int tid = threadIdx.x;
-    constexpr int NT = D / 32;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hf = lane >> 5;
     const float* Ac = p.A + w * (int64_t)(D * D);
-    for (int x = tid; x < D * D / 4; x += 256) {  // tile layout -> row-major
-        const float4 v = *(const float4*)(Ac + 4 * x);
-        const int e = 4 * x, m = e % 32, nn = (e / 32) % 32, tile = e / 1024;
-        const int i = 32 * (tile / NT) + m, j = 32 * (tile % NT) + nn;
-        sA[(i + 0) * D + j] = v.x;
-        sA[(i + 1) * D + j] = v.y;
-        sA[(i + 2) * D + j] = v.z;
-        sA[(i + 3) * D + j] = v.w;
-    }
+    for (int x = tid; x < D * D / 4; x += BLK / 32 * 64) *(float4*)(sA + 4 * x) = *(const float4*)(Ac + 4 * x);
     __syncthreads();
-    constexpr int TPT = 256 / BLK;  // threads per token
-    constexpr int JS = D / TPT;     // output columns per thread
-    const int64_t t = (int64_t)c * BLK + tid / TPT;
-    if (t >= p.n) return;
-    const int j0 = (tid % TPT) * JS;
-    const __bf16* Qr = (const __bf16*)p.q + (bh * p.n + t) * D;
-    float qv[D];
+    const int64_t t = (int64_t)c * BLK + 32 * wv + l32;  // this lane's token (B operand column)
+    const bool t_ok = t < p.n;
+    const __bf16* Qr = (const __bf16*)p.q + (bh * p.n + (t_ok ? t : 0)) * D;
+    constexpr int NT = D / 32;
+    f32x16 acc[NT];
 #pragma unroll
-    for (int x = 0; x < D / 8; ++x) {
-        const uint4 u = *(const uint4*)(Qr + 8 * x);
-        const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+    for (int nb = 0; nb < NT; ++nb) acc[nb] = f32x16{};
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            qv[8 * x + 2 * y] = __uint_as_float(wds[y] << 16);
-            qv[8 * x + 2 * y + 1] = __uint_as_float(wds[y] & 0xffff0000u);
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const int i0 = 16 * ks + 8 * hf;  // this lane's 8 values of i
+        const bf16x8 qb = t_ok ? *(const bf16x8*)(Qr + i0) : bf16x8{};
+#pragma unroll
+        for (int nb = 0; nb < NT; ++nb) {
+            // A_c^T row j = 32 nb + l32, i = i0 .. i0 + 7: tile (i / 32, j / 32), offset j % 32, i % 32
+            const float* src = sA + ((i0 / 32) * NT + nb) * 1024 + l32 * 32 + (i0 % 32);
+            const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
+            const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            bf16x8 ahi, alo;
+#pragma unroll
+            for (int y = 0; y < 8; ++y) {
+                ahi[y] = (__bf16)av[y];
+                alo[y] = (__bf16)(av[y] - (float)ahi[y]);
+            }
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, qb, acc[nb], 0, 0, 0);
+            acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, qb, acc[nb], 0, 0, 0);
         }
     }
-    float acc[JS];
+    if (!t_ok) return;
+    // lane holds token t and columns j = 32 nb + 8 r4 + 4 hf + (0..3)
+    __bf16* Or = (__bf16*)p.o + (bh * p.n + t) * D;
 #pragma unroll
-    for (int j = 0; j < JS; ++j) acc[j] = 0.f;
+    for (int nb = 0; nb < NT; ++nb)
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-        const float* ar = sA + i * D + j0;
-#pragma unroll
-        for (int j = 0; j < JS; j += 4) {
-            const float4 a = *(const float4*)(ar + j);
-            acc[j] = fmaf(qv[i], a.x, acc[j]);
-            acc[j + 1] = fmaf(qv[i], a.y, acc[j + 1]);
-            acc[j + 2] = fmaf(qv[i], a.z, acc[j + 2]);
-            acc[j + 3] = fmaf(qv[i], a.w, acc[j + 3]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int j = 32 * nb + 8 * r4 + 4 * hf;
+            const uint2 u = *(const uint2*)(Or + j);
+            *(uint2*)(Or + j) = make_uint2(
+                pack_bf16x2(__uint_as_float(u.x << 16) + acc[nb][4 * r4], __uint_as_float(u.x & 0xffff0000u) + acc[nb][4 * r4 + 1]),
+                pack_bf16x2(__uint_as_float(u.y << 16) + acc[nb][4 * r4 + 2], __uint_as_float(u.y & 0xffff0000u) + acc[nb][4 * r4 + 3]));
         }
-    }
-    __bf16* Or = (__bf16*)p.o + (bh * p.n + t) * D + j0;
-#pragma unroll
-    for (int j = 0; j < JS; j += 8) {
-        const uint4 u = *(const uint4*)(Or + j);
-        const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-        uint32_t outw[4];
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-            outw[y] = pack_bf16x2(__uint_as_float(wds[y] << 16) + acc[j + 2 * y],
-                                  __uint_as_float(wds[y] & 0xffff0000u) + acc[j + 2 * y + 1]);
-        *(uint4*)(Or + j) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-    }
+}
+
+template <int D, int BLK>
+hipError_t launch_states_t(const BsbrParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((bsbr_state_kernel<D, BLK>), dim3((unsigned)((int64_t)p.batch * p.heads_kv * p.nch)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
 }
 
 template <int D, int BLK>
 hipError_t launch_t(const BsbrParams& p, hipStream_t stream) {
-    const int64_t kv_chunks = (int64_t)p.batch * p.heads_kv * p.nch;
     const int64_t q_chunks = (int64_t)p.batch * p.heads_q * p.nch;
-    hipLaunchKernelGGL((bsbr_state_kernel<D, BLK>), dim3((unsigned)kv_chunks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bsbr_meta_kernel<D>), dim3((unsigned)q_chunks), dim3(64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bsbr_meta_kernel<D>), dim3((unsigned)q_chunks), dim3(64), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.nch > 1) {
         const int dd = D * D, slices = dd / kMixCols, groups = (p.nch + kMixRows - 1) / kMixRows;
-        const size_t lds = (size_t)kMixRows * p.nch * sizeof(float);
+        // dynamic LDS: the staged weights, at most 16 x (nch - 1) floats (<= 64 KiB at 1024 chunks)
+        const size_t lds = (size_t)kMixRows * (p.nch - 1) * sizeof(float);
         hipLaunchKernelGGL(bsbr_mix_kernel, dim3((unsigned)((int64_t)p.batch * p.heads_q * groups * slices)),
                            dim3(256), lds, stream, p, dd);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bsbr_apply_kernel<D, BLK>), dim3((unsigned)q_chunks), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((bsbr_apply_kernel<D, BLK>), dim3((unsigned)q_chunks), dim3(BLK / 32 * 64), 0, stream, p);
         e = hipGetLastError();
     }
     return e;
 }
 
 }  // namespace
+
+hipError_t launch_bsbr_states(const BsbrParams& p, int d, int chunk, hipStream_t stream) {
+    if (d == 128) return chunk == 128 ? launch_states_t<128, 128>(p, stream) : launch_states_t<128, 64>(p, stream);
+    return chunk == 128 ? launch_states_t<64, 128>(p, stream) : launch_states_t<64, 64>(p, stream);
+}
 
 hipError_t launch_bsbr_retrieval(const BsbrParams& p, int d, int chunk, hipStream_t stream) {
     if (d == 128) return chunk == 128 ? launch_t<128, 128>(p, stream) : launch_t<128, 64>(p, stream);
