@@ -19,8 +19,9 @@ Also reported, outside the timed region: the backward pass (BF1 and dense route)
 tensors as a key/value cache (batch 1 and 16; persistent plan, plan per token, dense route), the
 topology sweep (BF1 against the local sliding band
 and the static-random graph at the nearest selected-pair count, same inputs, with each graph's
-communication depth) and the forward alone on the other workloads, each against the roofline
-that bounds it (HBM bytes, matrix-core flops or vector flops).
+communication depth), the forward alone on the other workloads, each against the roofline
+that bounds it (HBM bytes, matrix-core flops or vector flops), and BSBR attention (within-chunk
+term plus the retrieval over earlier chunks' states) on the 8K-token block-diagonal workload.
 
 Prints ONE JSON line.  value = selected-interaction TFLOP/s of the step, where selected FLOPs =
 4 * d * batch * heads_q * S and S counts the causal token pairs the route selects (QK^T and PV
@@ -315,6 +316,41 @@ def other_workloads(names, steps: int) -> dict:
     return out
 
 
+def bsbr_bench(steps: int) -> dict:
+    """BSBR attention on the bsbr_chunk_8k workload (2 x 8 heads, n 8192, d 64, chunks of 128):
+    the within-chunk term alone (the forward over the block-diagonal route) and the whole operator
+    with the retrieval over earlier chunks' states.  HBM-bound by its algorithmic bytes (Q, K, V, O,
+    meta queries and keys once); the retrieval's flops are the chunk states (2 n d^2 per key/value
+    head), the mix (nch (nch - 1) d^2 per query head) and the read-out (2 n d^2 per query head)."""
+    import torch
+    import long_context_block_amd as bsa
+    import synth
+    w = synth.WORKLOADS["bsbr_chunk_8k"]
+    q, k, v = (x.cuda() for x in synth.make_qkv(w))
+    r, h = (x.cuda() for x in synth.make_meta(w))
+    o = torch.empty_like(q)
+    ws = torch.empty(bsa.bsa_bsbr_workspace_bytes(w.batch, w.heads_q, w.heads_kv, w.n, w.d, w.block),
+                     dtype=torch.uint8, device=q.device)
+    rp, ci = bsa.build_route(bsa.route_spec(bsa.BSA_ROUTE_BLOCK_DIAGONAL), w.n, w.block)
+    steps = max(20, steps)
+    ms_within = time_loop(lambda: bsa.bsa_forward(q, k, v, o, rp, ci, w.block), steps, 5)
+    ms = time_loop(lambda: bsa.bsa_bsbr_forward(q, k, v, r, h, o, w.block, ws), steps, 5)
+    nch = -(-w.n // w.block)
+    nbytes = algorithmic_bytes(w) + 2 * w.batch * nch * w.d * (w.heads_q + w.heads_kv)
+    flops_ret = (2.0 * w.n * w.d * w.d * w.batch * w.heads_kv + nch * (nch - 1) * w.d * w.d * w.batch * w.heads_q
+                 + 2.0 * w.n * w.d * w.d * w.batch * w.heads_q)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {"workload": w.name, "chunks": nch, "ms": round(ms, 5), "within_chunk_ms": round(ms_within, 5),
+           "retrieval_ms": round(ms - ms_within, 5), "retrieval_flops": flops_ret,
+           "algorithmic_bytes": int(nbytes), "algorithmic_GBs": round(gbs, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)},
+           "workspace_bytes": int(ws.numel())}
+    del q, k, v, r, h, o, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
     """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload."""
     from oracle import attn as A
@@ -487,6 +523,7 @@ def main():
         out["decode"] = [decode_bench(w, kd, vd, args.steps, batch) for batch in (1, 16)]
         out["backward"] = backward_bench(w, qd, kd, vd, args.steps)
         out["other_workloads"] = other_workloads([x for x in synth.WORKLOADS if x != w.name], args.steps)
+        out["bsbr"] = bsbr_bench(args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)
     print(json.dumps(out), flush=True)
