@@ -235,13 +235,14 @@ size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d);
  *     F_c = K_c^T V_c (d x d, the chunk's tokens),  W[c, :] = softmax over c' < c of
  *     scale * R_c . H_c'  (chunk 0 retrieves nothing).
  *
- * The within-chunk term is bsa_forward over the block-diagonal route (built in the workspace).
+ * The within-chunk term is the causal block-diagonal attention (bsa_forward with the
+ * block-diagonal route computes the same term); both terms are formed by one kernel per chunk.
  * Inputs (device, caller-owned, contiguous, 16-byte aligned, bf16): q [batch, heads_q, n, d];
  * k, v [batch, heads_kv, n, d]; r_meta (meta queries) [batch, heads_q, nch, d]; h_meta (meta
  * keys) [batch, heads_kv, nch, d].  Output o like q.  scale <= 0 selects 1/sqrt(d) for both
- * softmaxes.  workspace: at least bsa_bsbr_workspace_bytes(...) bytes (the route, fp32 chunk
- * states, meta weights and retrieved states); contents on entry do not matter.  Supported: BF16;
- * d in {64, 128}; chunk in {64, 128}; 1 <= nch <= 1024.  Six kernels on `stream`, no atomics.
+ * softmaxes.  workspace: at least bsa_bsbr_workspace_bytes(...) bytes (fp32 chunk states, meta
+ * weights and retrieved states); contents on entry do not matter.  Supported: BF16; d in
+ * {64, 128}; chunk in {64, 128}; 1 <= nch <= 1024.  Four kernels on `stream`, no atomics.
  * Errors: BSA_ERR_INVALID_ARGUMENT (NULL or misaligned pointers, bad sizes), BSA_ERR_UNSUPPORTED
  * (dtype, d, chunk, nch), BSA_ERR_CAPACITY (workspace), BSA_ERR_DEVICE (launch failure).
  */

@@ -353,7 +353,7 @@ size_t bsa_bsbr_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv
                                 int32_t chunk) {
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || n < 1 || d < 1 || chunk < 1) return 0;
     const size_t nch = (size_t)((n + chunk - 1) / chunk);
-    return align256((2 * nch + 1) * sizeof(int32_t)) + align256((size_t)batch * heads_kv * nch * d * d * sizeof(float)) +
+    return align256((size_t)batch * heads_kv * nch * d * d * sizeof(float)) +
            align256((size_t)batch * heads_q * nch * nch * sizeof(float) + 64) +
            (size_t)batch * heads_q * nch * d * d * sizeof(float);
 }
@@ -387,9 +387,6 @@ bsa_status bsa_bsbr_forward(const void* q, const void* k, const void* v, const v
         return fail(BSA_ERR_UNSUPPORTED, "grid too large");
     char* ws = (char*)workspace;
     bsa::BsbrParams p;
-    p.route_rp = (int32_t*)ws;
-    p.route_ci = p.route_rp + nch + 1;
-    ws += align256((size_t)(2 * nch + 1) * sizeof(int32_t));
     p.q = q; p.k = k; p.v = v; p.r = r_meta; p.h = h_meta; p.o = o;
     p.F = (float*)ws;
     ws += align256((size_t)batch * heads_kv * nch * d * d * sizeof(float));
@@ -399,15 +396,8 @@ bsa_status bsa_bsbr_forward(const void* q, const void* k, const void* v, const v
     p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.nch = (int32_t)nch; p.n = n;
     const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
     p.scale_log2 = (float)(sc * 1.4426950408889634073599);
-    // chunk states and the block-diagonal route, then the within-chunk term (the forward over that
-    // route), then the retrieval added to its output
-    hipError_t e = bsa::launch_bsbr_states(p, d, chunk, stream);
-    if (e != hipSuccess) return device_error(e, "BSBR chunk-state launch");
-    bsa_status s = run_forward(q, k, v, o, nullptr, batch, heads_q, heads_kv, n, d, chunk, dtype, scale, p.route_rp,
-                               p.route_ci, nch, stream);
-    if (s != BSA_OK) return s;
-    e = bsa::launch_bsbr_retrieval(p, d, chunk, stream);
-    if (e != hipSuccess) return device_error(e, "BSBR retrieval launch");
+    const hipError_t e = bsa::launch_bsbr(p, d, chunk, stream);
+    if (e != hipSuccess) return device_error(e, "BSBR launch");
     return ok();
 }
 

@@ -120,20 +120,15 @@ struct BsbrParams {
     const void* v;
     const void* r;    // meta queries [batch, heads_q, nch, d]
     const void* h;    // meta keys [batch, heads_kv, nch, d]
-    void* o;          // [batch, heads_q, n, d]: holds the within-chunk term, receives the sum
+    void* o;          // [batch, heads_q, n, d]
     float* F;         // workspace: chunk states [batch, heads_kv, nch, d * d] (32 x 32 tiles)
     float* W;         // workspace: meta weights [batch, heads_q, nch, nch]
     float* A;         // workspace: retrieved states [batch, heads_q, nch, d * d]
-    int32_t* route_rp;// workspace: block-diagonal route of the within-chunk term [nch + 1]
-    int32_t* route_ci;// [nch]
     int32_t batch, heads_q, heads_kv, nch;
     int64_t n;
     float scale_log2;
 };
-// chunk states (and the block-diagonal route), then — after the within-chunk forward — the
-// meta weights, the mix and the read-out added to the output
-hipError_t launch_bsbr_states(const BsbrParams& p, int d, int chunk, hipStream_t stream);
-hipError_t launch_bsbr_retrieval(const BsbrParams& p, int d, int chunk, hipStream_t stream);
+hipError_t launch_bsbr(const BsbrParams& p, int d, int chunk, hipStream_t stream);
 
 int64_t bwd_segments_upper_bound(int64_t nqb, int64_t nnz, int heads_q, int heads_kv, int block);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, int block, hipStream_t stream);
