@@ -200,8 +200,9 @@ def topology_sweep(w, qd, kd, vd, steps: int) -> dict:
 def decode_bench(w, kd, vd, steps: int, batch: int = 1) -> dict:
     """Selected-page decode on the workload's key/value tensors as a cache (newest token at the
     last position): with the route built once for the cache (persistent plan), with the plan
-    rebuilt for every token (the pages' per-token accounting, "BF1 ...", section 5), and over
-    the dense causal route (the speedup denominator).  Algorithmic bytes: the selected key and
+    rebuilt for every token (the pages' per-token accounting, "BF1 ...", section 5), with the
+    row generated in the kernel (bsa_decode_routed: no plan at all), and over the dense causal
+    route (the speedup denominator).  Algorithmic bytes: the selected key and
     value rows, q and o."""
     import torch
     import long_context_block_amd as bsa
@@ -229,6 +230,10 @@ def decode_bench(w, kd, vd, steps: int, batch: int = 1) -> dict:
                "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        # the same decode with the row generated inside the kernel from the route's closed form
+        # (no route in memory, no planning launch)
+        routed = lambda: bsa.bsa_decode_routed(q, kc, vc, o, sl, spec, w.block, ws)  # noqa: E731
+        rec["ms_routed"] = round(time_loop(routed, max(50, steps), 10), 5)
         if name == "bf1":
             def planned():
                 bsa.bsa_build_route(spec, w.n, w.block, rp, ci)

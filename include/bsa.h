@@ -227,6 +227,26 @@ bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, v
 size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d);
 
 /*
+ * bsa_decode_routed — bsa_decode with the route given by its parameters instead of a CSR
+ * route: each sequence's row R(i) is generated inside the kernel from the closed form of the
+ * kind (the sets documented at bsa_route_kind), so a decode step needs no route in memory and
+ * no planning launch ("BF1 ...", section 4: topology/planning cost kept apart from the
+ * attention kernel; here that cost is zero).  Same arguments, layout, arithmetic and output as
+ * bsa_decode, with `spec` (host pointer, read during the call only) in place of row_ptr,
+ * col_idx and nnz.  Kinds: BF1, block-diagonal, dense causal, sliding window; static-random
+ * returns BSA_ERR_UNSUPPORTED (its rows come from a per-row selection: build the route with
+ * bsa_build_route and call bsa_decode), an unknown kind or n_local < 0 BSA_ERR_INVALID_ARGUMENT.
+ * The output equals bsa_decode's with the route bsa_build_route writes for the same spec,
+ * bit for bit when both calls choose the same number of key splits (the split count follows
+ * the average row of a CSR route and the row of a full cache here).  Two kernels on `stream`.
+ */
+bsa_status bsa_decode_routed(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                             int64_t n_max, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                             const bsa_route_spec* spec, float* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
  * bsa_bsbr_forward — BSBR attention ("bsbr", Solution: the combined formula), chunks of
  * `chunk` tokens, nch = ceil(n / chunk):
  *

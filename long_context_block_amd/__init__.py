@@ -33,7 +33,7 @@ BSA_ROUTE_STATIC_RANDOM = 3
 BSA_ROUTE_SLIDING_WINDOW = 4
 
 EXPORTS = ("bsa_build_route", "bsa_forward", "bsa_dense_causal_ref", "bsa_dense_route_workspace_bytes",
-           "bsa_decode", "bsa_decode_workspace_bytes", "bsa_build_route_transpose", "bsa_backward",
+           "bsa_decode", "bsa_decode_routed", "bsa_decode_workspace_bytes", "bsa_build_route_transpose", "bsa_backward",
            "bsa_backward_workspace_bytes", "bsa_bsbr_forward", "bsa_bsbr_workspace_bytes", "bsa_check_route",
            "bsa_status_string", "bsa_last_error")
 
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.bsa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, ctypes.c_int, f32, vp, vp,
                                  i64, vp, ctypes.c_size_t, vp]
         L.bsa_decode.restype = ctypes.c_int
+        L.bsa_decode_routed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, ctypes.c_int, f32,
+                                        ctypes.POINTER(bsa_route_spec), vp, ctypes.c_size_t, vp]
+        L.bsa_decode_routed.restype = ctypes.c_int
         L.bsa_decode_workspace_bytes.argtypes = [i32, i32, i32]
         L.bsa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.bsa_build_route_transpose.argtypes = [vp, vp, i64, i64, vp, vp, vp]
@@ -242,6 +245,28 @@ def bsa_decode(q, k_cache, v_cache, o, seq_lens, row_ptr, col_idx, block: int, w
                             wp, workspace.numel() * 4, _stream(stream)))
 
 
+def bsa_decode_routed(q, k_cache, v_cache, o, seq_lens, spec: bsa_route_spec, block: int, workspace,
+                      scale: float = 0.0, lse=None, stream=None) -> None:
+    """bsa_decode with the route rows generated in the kernel from `spec` (no CSR route)."""
+    import torch
+    dt = _dtype_code(q)
+    b, hq, d = q.shape
+    hkv, n_max = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (b, hkv, n_max, d) or tuple(v_cache.shape) != (b, hkv, n_max, d) or \
+            tuple(o.shape) != (b, hq, d):
+        raise ValueError("shape mismatch between q, k_cache, v_cache and o")
+    if tuple(seq_lens.shape) != (b,):
+        raise ValueError("seq_lens must have shape [b]")
+    ptrs = [_dev_ptr(x, nm, q.dtype) for x, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (o, "o"))]
+    if lse is not None and tuple(lse.shape) != (b, hq):
+        raise ValueError("lse must have shape [b, Hq]")
+    lp = _dev_ptr(lse, "lse", torch.float32, allow_none=True)
+    sp = _dev_ptr(seq_lens, "seq_lens", torch.int32)
+    wp = _dev_ptr(workspace, "workspace", torch.float32)
+    _check(lib().bsa_decode_routed(*ptrs, lp, sp, b, hq, hkv, n_max, d, block, dt, float(scale),
+                                   ctypes.byref(spec), wp, workspace.numel() * 4, _stream(stream)))
+
+
 def bsa_build_route_transpose(row_ptr, col_idx, t_row_ptr, t_col_idx, stream=None) -> None:
     """Write the transposed route (readers of every key block) into t_row_ptr/t_col_idx (int32 GPU)."""
     import torch
@@ -365,6 +390,18 @@ def decode(q, k_cache, v_cache, seq_lens, row_ptr, col_idx, block: int, scale: f
     lse = torch.empty(b, hq, dtype=torch.float32, device=q.device) if with_lse else None
     ws = torch.empty(max(1, bsa_decode_workspace_bytes(b, hq, d) // 4), dtype=torch.float32, device=q.device)
     bsa_decode(q, k_cache, v_cache, o, seq_lens, row_ptr, col_idx, block, ws, scale, lse, stream)
+    return (o, lse) if with_lse else o
+
+
+def decode_routed(q, k_cache, v_cache, seq_lens, spec: bsa_route_spec, block: int, scale: float = 0.0,
+                  with_lse: bool = False, stream=None):
+    """Allocate the output, LSE and workspace and run bsa_decode_routed."""
+    import torch
+    b, hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty(b, hq, dtype=torch.float32, device=q.device) if with_lse else None
+    ws = torch.empty(max(1, bsa_decode_workspace_bytes(b, hq, d) // 4), dtype=torch.float32, device=q.device)
+    bsa_decode_routed(q, k_cache, v_cache, o, seq_lens, spec, block, ws, scale, lse, stream)
     return (o, lse) if with_lse else o
 
 

@@ -287,11 +287,14 @@ size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d) {
     return (size_t)batch * heads_q * bsa::kDecodeMaxSplits * (d + 2) * sizeof(float);
 }
 
-bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                      const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n_max,
-                      int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
-                      const int32_t* col_idx, int64_t nnz, float* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+namespace {
+
+// Shared by bsa_decode (CSR route: row_ptr/col_idx/nnz) and bsa_decode_routed (spec).
+bsa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                       const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n_max,
+                       int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
+                       const int32_t* col_idx, int64_t nnz, const bsa_route_spec* spec, float* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || n_max < 1 || block < 1 || d < 1)
         return fail(BSA_ERR_INVALID_ARGUMENT,
                     "sizes must satisfy batch >= 0, heads >= 1, n_max >= 1, d >= 1, block >= 1 "
@@ -305,30 +308,44 @@ bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, v
     if (!(scale <= 0.f) && !std::isfinite(scale)) return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be finite");
     const int64_t nqb = (n_max + block - 1) / block;
     if (nqb > INT32_MAX - 1) return fail(BSA_ERR_UNSUPPORTED, "too many blocks (%lld)", (long long)nqb);
+    if (spec) {
+        if (spec->kind < BSA_ROUTE_BF1 || spec->kind > BSA_ROUTE_SLIDING_WINDOW)
+            return fail(BSA_ERR_INVALID_ARGUMENT, "unknown route kind %d", spec->kind);
+        if (spec->kind == BSA_ROUTE_STATIC_RANDOM)
+            return fail(BSA_ERR_UNSUPPORTED, "static-random rows have no closed form: build the route and use bsa_decode");
+        if (spec->n_local < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "n_local must be >= 0");
+    }
     if (batch == 0) return ok();
-    if (!q || !k_cache || !v_cache || !o || !seq_lens || !row_ptr || !col_idx || !workspace)
+    if (!q || !k_cache || !v_cache || !o || !seq_lens || !workspace || (!spec && (!row_ptr || !col_idx)))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o, seq_lens, route and workspace must be non-NULL");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o and workspace must be 16-byte aligned");
     if (lse && ((uintptr_t)lse & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
     if (((uintptr_t)seq_lens & 3u) != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
-    if (nnz < nqb || nnz > INT32_MAX)
+    if (!spec && (nnz < nqb || nnz > INT32_MAX))
         return fail(BSA_ERR_INVALID_ARGUMENT, "nnz=%lld must be in [nqb=%lld, 2^31)", (long long)nnz, (long long)nqb);
     const size_t need = bsa_decode_workspace_bytes(batch, heads_q, d);
     if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
 
     bsa::DecodeParams p;
     p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
-    p.seq_lens = seq_lens; p.row_ptr = row_ptr; p.col_idx = col_idx; p.ws = workspace;
+    p.seq_lens = seq_lens; p.row_ptr = spec ? nullptr : row_ptr; p.col_idx = spec ? nullptr : col_idx;
+    p.ws = workspace;
+    p.rkind = spec ? spec->kind : -1;
+    p.n_local = spec ? spec->n_local : 0;
+    p.keep_first = spec ? (spec->keep_first != 0) : 0;
     p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.block = block;
-    p.n_max = n_max; p.nnz = nnz;
+    p.n_max = n_max; p.nnz = spec ? 0 : nnz;
     const int G = heads_q / heads_kv;
     p.gc = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     p.hchunks = G / p.gc;
     // Splits: enough single-wavefront units to cover the device (~1024), but no more than the
-    // 32-key sub-blocks of an average row (the rows of these routes are of similar length).
+    // 32-key sub-blocks of a typical row: the average row of a CSR route (the rows of these
+    // routes are of similar length), the row of a full cache for a closed-form one.
     const int64_t base_units = (int64_t)batch * heads_kv * p.hchunks;
-    const int64_t avg_sub = ((nnz + nqb - 1) / nqb) * (block / 32);
+    const int64_t row_blocks = spec ? bsa::route_row_count(spec->kind, nqb - 1, spec->n_local, p.keep_first, 0)
+                                    : (nnz + nqb - 1) / nqb;
+    const int64_t avg_sub = row_blocks * (block / 32);
     int64_t S = (1024 + base_units - 1) / base_units;
     S = S < avg_sub ? S : avg_sub;
     S = S < 1 ? 1 : (S > bsa::kDecodeMaxSplits ? bsa::kDecodeMaxSplits : S);
@@ -340,6 +357,27 @@ bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, v
     const hipError_t e = bsa::launch_decode(p, d, dtype == BSA_BF16, stream);
     if (e != hipSuccess) return device_error(e, "decode launch");
     return ok();
+}
+
+}  // namespace
+
+bsa_status bsa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                      const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n_max,
+                      int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
+                      const int32_t* col_idx, int64_t nnz, float* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    return decode_impl(q, k_cache, v_cache, o, lse, seq_lens, batch, heads_q, heads_kv, n_max, d, block, dtype,
+                       scale, row_ptr, col_idx, nnz, nullptr, workspace, workspace_bytes, stream);
+}
+
+bsa_status bsa_decode_routed(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                             const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                             int64_t n_max, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                             const bsa_route_spec* spec, float* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    if (!spec) return fail(BSA_ERR_INVALID_ARGUMENT, "spec must be non-NULL");
+    return decode_impl(q, k_cache, v_cache, o, lse, seq_lens, batch, heads_q, heads_kv, n_max, d, block, dtype,
+                       scale, nullptr, nullptr, 0, spec, workspace, workspace_bytes, stream);
 }
 
 size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block) {

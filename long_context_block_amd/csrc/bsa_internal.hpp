@@ -42,6 +42,37 @@ __host__ __device__ inline int64_t route_row_count(int kind, int64_t i, int n_lo
     }
 }
 
+// Entry idx (0 <= idx < route_row_count) of row i, ascending, for the routes whose rows have a
+// closed form: BF1, block-diagonal, dense causal and sliding window (not static-random, whose
+// rows come from a per-row selection).  BF1 with i > n_local lists, in ascending order, block 0
+// when keep_first adds it (i not a power of two), the dyadic blocks i - 2^k left of the window
+// (2^k > n_local, k from floor(log2 i) down), then the window i - n_local .. i; with i <= n_local
+// the window reaches block 0 and the row is 0 .. i.
+__host__ __device__ inline int64_t route_row_entry(int kind, int64_t i, int n_local, int keep_first, int64_t idx) {
+    switch (kind) {
+    case BSA_ROUTE_BLOCK_DIAGONAL:
+        return i;
+    case BSA_ROUTE_DENSE_CAUSAL:
+        return idx;
+    case BSA_ROUTE_SLIDING_WINDOW:
+        return (i > n_local ? i - n_local : 0) + idx;
+    case BSA_ROUTE_BF1: {
+        if (i <= n_local) return idx;
+        if (keep_first && !is_pow2(i)) {
+            if (idx == 0) return 0;
+            --idx;
+        }
+        const int kmax = floor_log2_u64((uint64_t)i);
+        const int kmin = n_local == 0 ? 0 : floor_log2_u64((uint64_t)n_local) + 1;  // 2^kmin > n_local
+        const int64_t nd = kmax >= kmin ? kmax - kmin + 1 : 0;
+        if (idx < nd) return i - ((int64_t)1 << (kmax - idx));
+        return i - n_local + (idx - nd);
+    }
+    default:
+        return -1;
+    }
+}
+
 // Launchers (defined in the kernel translation units).  They only enqueue work and return
 // the hipError_t of the launch.
 hipError_t launch_route_build(const bsa_route_spec& spec, int64_t nqb, int32_t* row_ptr,
@@ -71,9 +102,11 @@ struct DecodeParams {
     void* o;        // [batch, heads_q, d]
     float* lse;     // [batch, heads_q] or null
     const int32_t* seq_lens;
-    const int32_t* row_ptr;
+    const int32_t* row_ptr;  // CSR route (rkind < 0)
     const int32_t* col_idx;
     float* ws;      // [batch, heads_q, splits, d + 2] partials
+    int32_t rkind;  // < 0: rows from row_ptr/col_idx; else a closed-form bsa_route_kind
+    int32_t n_local, keep_first;
     int32_t batch, heads_q, heads_kv, block;
     int32_t splits;   // split units per (b, kv head, head group), <= kDecodeMaxSplits
     int32_t hchunks;  // query-head groups per kv head

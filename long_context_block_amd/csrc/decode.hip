@@ -67,9 +67,16 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 
     const int64_t t = clamp_len(p.seq_lens[b], p.n_max) - 1;
     const int i = (int)(t / p.block);
-    int e0 = p.row_ptr[i], e1 = p.row_ptr[i + 1];
-    e0 = e0 < 0 ? 0 : (e0 > p.nnz ? (int)p.nnz : e0);
-    e1 = e1 < e0 ? e0 : (e1 > p.nnz ? (int)p.nnz : e1);
+    const bool csr = p.rkind < 0;
+    int e0 = 0, e1 = 0;
+    if (csr) {
+        e0 = p.row_ptr[i];
+        e1 = p.row_ptr[i + 1];
+        e0 = e0 < 0 ? 0 : (e0 > p.nnz ? (int)p.nnz : e0);
+        e1 = e1 < e0 ? e0 : (e1 > p.nnz ? (int)p.nnz : e1);
+    } else {
+        e1 = (int)route_row_count(p.rkind, i, p.n_local, p.keep_first, 0);
+    }
     const int sh = p.block == 128 ? 2 : 1;  // log2 of the 32-key sub-blocks per block
     const int nsub = (e1 - e0) << sh;
 
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     // skipped
     auto next_sub = [&](int& sb) -> int64_t {
         for (; sb < nsub; sb += p.splits) {
-            const int j = p.col_idx[e0 + (sb >> sh)];
+            const int j = csr ? p.col_idx[e0 + (sb >> sh)]
+                              : (int)route_row_entry(p.rkind, i, p.n_local, p.keep_first, sb >> sh);
             if (j < 0 || j > i) continue;
             const int64_t k0 = (int64_t)j * p.block + ((sb & ((1 << sh) - 1)) << 5);
             if (k0 <= t) return k0;

@@ -111,6 +111,47 @@ def test_decode_workspace_and_empty_batch():
     assert _raw_decode(batch=0, q=None, k=None, v=None, o=None, sl=None, ws=None) == bsa.BSA_OK
 
 
+def _raw_decode_routed(spec=None, **kw):
+    args = dict(q=16, k=16, v=16, o=16, lse=None, sl=16, batch=2, hq=4, hkv=2, n_max=1000, d=128, block=128,
+                dtype=0, scale=0.0, ws=16, wsb=None, stream=None)
+    args.update(kw)
+    if args["wsb"] is None:
+        args["wsb"] = bsa.bsa_decode_workspace_bytes(args["batch"], args["hq"], args["d"])
+    sp = ctypes.byref(spec) if spec is not None else None
+    return bsa.lib().bsa_decode_routed(args["q"], args["k"], args["v"], args["o"], args["lse"], args["sl"],
+                                       args["batch"], args["hq"], args["hkv"], args["n_max"], args["d"],
+                                       args["block"], args["dtype"], args["scale"], sp, args["ws"], args["wsb"],
+                                       args["stream"])
+
+
+@pytest.mark.parametrize("spec,kw,status", [
+    (None, {}, bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_STATIC_RANDOM), {}, bsa.BSA_ERR_UNSUPPORTED),
+    (bsa.route_spec(bsa.BSA_ROUTE_STATIC_RANDOM), dict(batch=0), bsa.BSA_ERR_UNSUPPORTED),
+    (bsa.route_spec(9), {}, bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(-1), {}, bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1, n_local=-2), {}, bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1), dict(hq=3, hkv=2), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1), dict(d=96), bsa.BSA_ERR_UNSUPPORTED),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1), dict(block=32), bsa.BSA_ERR_UNSUPPORTED),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1), dict(sl=None), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_BF1), dict(q=24), bsa.BSA_ERR_INVALID_ARGUMENT),
+    (bsa.route_spec(bsa.BSA_ROUTE_DENSE_CAUSAL), dict(wsb=100), bsa.BSA_ERR_CAPACITY),
+    (bsa.route_spec(bsa.BSA_ROUTE_SLIDING_WINDOW), dict(scale=float("inf")), bsa.BSA_ERR_INVALID_ARGUMENT),
+])
+def test_decode_routed_rejects_bad_arguments(spec, kw, status):
+    assert _raw_decode_routed(spec, **kw) == status
+    assert bsa.bsa_last_error() != ""
+
+
+def test_decode_routed_empty_batch_and_no_route_pointers():
+    # no CSR arrays at all: the closed-form kinds validate and an empty batch is a no-op
+    for kind in (bsa.BSA_ROUTE_BF1, bsa.BSA_ROUTE_BLOCK_DIAGONAL, bsa.BSA_ROUTE_DENSE_CAUSAL,
+                 bsa.BSA_ROUTE_SLIDING_WINDOW):
+        assert _raw_decode_routed(bsa.route_spec(kind), batch=0, q=None, k=None, v=None, o=None, sl=None,
+                                  ws=None) == bsa.BSA_OK
+
+
 def test_dense_ref_rejects_small_workspace():
     L = bsa.lib()
     need = bsa.bsa_dense_route_workspace_bytes(4096, 64)

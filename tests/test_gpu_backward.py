@@ -17,6 +17,7 @@ import long_context_block_amd as bsa
 from oracle import attn as A
 from oracle import routes as R
 import synth
+from route_ref import routes, workload_routes
 
 pytestmark = pytest.mark.gpu
 
@@ -38,10 +39,10 @@ def transpose_sets(rp, ci):
 def test_route_transpose_bit_exact(kind, n, B):
     if kind == R.DENSE_CAUSAL and n > 5000:
         pytest.skip("dense route at 256 blocks is covered at the smaller sizes")
-    rp, ci = bsa.build_route(bsa.route_spec(kind), n, B)
+    (rp, ci), (orp, oci) = routes(kind, n, B)
     trp, tci = bsa.build_route_transpose(rp, ci)
     torch.cuda.synchronize()
-    want_rp, want_ci = R.to_csr(transpose_sets(rp.cpu().numpy(), ci.cpu().numpy()))
+    want_rp, want_ci = R.to_csr(transpose_sets(orp, oci))
     assert np.array_equal(trp.cpu().numpy(), want_rp) and np.array_equal(tci.cpu().numpy(), want_ci)
 
 
@@ -56,12 +57,12 @@ def run_backward(w, kind=None, seed=61, q_rows=None, k_rows=None):
     q, k, v = synth.make_qkv(w)
     g = torch.Generator("cpu").manual_seed(seed)
     d_o = torch.randn(q.shape, generator=g).to(q.dtype)
-    rp, ci = bsa.build_route(bsa.route_spec(kind, w.n_local, w.keep_first, w.n_random, w.route_seed), w.n, w.block)
+    (rp, ci), (orp, oci) = workload_routes(w, kind)
     qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), d_o.cuda()
     o, lse = bsa.forward(qd, kd, vd, rp, ci, w.block, with_lse=True)
     dq, dk, dv = bsa.backward(qd, kd, vd, o, dod, lse, rp, ci, w.block)
     torch.cuda.synchronize()
-    rq, rk, rv = A.attention_backward(q, k, v, d_o, w.block, rp.cpu().numpy(), ci.cpu().numpy(),
+    rq, rk, rv = A.attention_backward(q, k, v, d_o, w.block, orp, oci,
                                       q_rows=q_rows, k_rows=k_rows)
     if q_rows is not None:
         dq = dq[:, :, q_rows]
@@ -146,7 +147,7 @@ def test_backward_transposed_rows_in_any_order(wname, n):
     q, k, v = synth.make_qkv(w)
     g = torch.Generator("cpu").manual_seed(62)
     d_o = torch.randn(q.shape, generator=g).to(q.dtype)
-    rp, ci = bsa.build_route(bsa.route_spec(w.route_kind, w.n_local, w.keep_first, w.n_random, w.route_seed), w.n, w.block)
+    (rp, ci), (orp, oci) = workload_routes(w)
     trp, tci = bsa.build_route_transpose(rp, ci)
     trp_h, tci_h = trp.cpu().numpy(), tci.cpu().numpy().copy()
     for j in range(len(trp_h) - 1):
@@ -162,7 +163,7 @@ def test_backward_transposed_rows_in_any_order(wname, n):
         bsa.bsa_backward(qd, kd, vd, o, dod, lse, dq, dk, dv, rp, ci, trp, t_ci, w.block, ws)
         grads.append((dq, dk, dv))
     torch.cuda.synchronize()
-    ref = A.attention_backward(q, k, v, d_o, w.block, rp.cpu().numpy(), ci.cpu().numpy())
+    ref = A.attention_backward(q, k, v, d_o, w.block, orp, oci)
     for name, got, r in zip(("dq", "dk", "dv"), grads[1], ref):
         rl2, mx = grad_errors(got, r)
         print(f"  reversed rows {name}: rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)

@@ -13,6 +13,7 @@ import long_context_block_amd as bsa
 from oracle import attn as A
 from oracle import routes as R
 import synth
+from route_ref import routes
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +39,11 @@ def make(batch, hq, hkv, n_max, d, dtype, seed):
 
 def run(q, k, v, lens, kind, B, n_local=2, n_random=14, with_lse=True):
     n_max = k.shape[2]
-    rp, ci = bsa.build_route(bsa.route_spec(kind, n_local, 1, n_random, 17), n_max, B)
+    (rp, ci), oracle_rc = routes(kind, n_max, B, n_local, 1, n_random, 17)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     o, lse = bsa.decode(q.cuda(), k.cuda(), v.cuda(), sl, rp, ci, B, with_lse=True)
     torch.cuda.synchronize()
-    return o.float().cpu().numpy(), lse.cpu().numpy(), (rp.cpu().numpy(), ci.cpu().numpy())
+    return o.float().cpu().numpy(), lse.cpu().numpy(), oracle_rc
 
 
 CASES = [
@@ -134,3 +135,80 @@ def test_decode_errors():
     assert e.value.status == bsa.BSA_ERR_UNSUPPORTED
     with pytest.raises(ValueError):  # a route built for a shorter cache is refused by the binding
         bsa.bsa_decode(q, k, k, torch.empty_like(q), sl, *bsa.build_route(bsa.route_spec(R.BF1), 64, 64), 64, ws)
+
+
+ROUTED_KINDS = [R.BF1, R.BLOCK_DIAGONAL, R.DENSE_CAUSAL, R.SLIDING_WINDOW]
+
+
+def run_routed(q, k, v, lens, kind, B, n_local=2, keep_first=1):
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    spec = bsa.route_spec(kind, n_local, keep_first)
+    o, lse = bsa.decode_routed(q.cuda(), k.cuda(), v.cuda(), sl, spec, B, with_lse=True)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("kind", ROUTED_KINDS)
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_decode_routed_parity(case, kind):
+    # rows generated in the kernel from the route's closed form, against the oracle's route
+    name, batch, hq, hkv, n_max, d, B, dt = case
+    q, k, v = make(batch, hq, hkv, n_max, d, dt, seed=34)
+    lens = [n_max, 1, B + 1, B, n_max // 2 + 3][:batch]
+    print(f"decode_routed {name} kind={kind} lens={lens}", flush=True)
+    o, lse = run_routed(q, k, v, lens, kind, B)
+    rp, ci = R.route_csr(kind, n_max, B, n_local=2, keep_first=True)
+    ref, ref_lse = A.decode_attention(q, k, v, lens, B, rp, ci, return_lse=True)
+    mx, rl2 = errors(o.float().cpu().numpy(), ref)
+    ma, rt = tol(dt)
+    assert mx <= ma and rl2 <= rt, (mx, rl2)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= (1e-5 if dt == torch.float32 else 1e-4)
+
+
+@pytest.mark.parametrize("kind,n_local,keep_first", [(R.BF1, 2, 1), (R.BF1, 0, 0), (R.BF1, 5, 1),
+                                                     (R.BLOCK_DIAGONAL, 2, 1), (R.DENSE_CAUSAL, 2, 1),
+                                                     (R.SLIDING_WINDOW, 3, 1), (R.SLIDING_WINDOW, 0, 0)])
+def test_decode_routed_bit_equal_to_the_csr_route(kind, n_local, keep_first):
+    # 512 (sequence, kv head) units: both entry points use 2 key splits, so their sums run in the
+    # same order and the outputs agree bit for bit (lengths from 1 to the full cache)
+    batch, hq, hkv, n_max, d, B = 64, 8, 8, 700, 64, 64
+    q, k, v = make(batch, hq, hkv, n_max, d, torch.bfloat16, seed=35)
+    lens = [1 + (37 * x * x + 11 * x) % n_max for x in range(batch)]
+    lens[:4] = [1, B, B + 1, n_max]
+    print(f"decode_routed vs csr kind={kind} n_local={n_local} keep_first={keep_first}", flush=True)
+    o1, l1 = run_routed(q, k, v, lens, kind, B, n_local, keep_first)
+    (rp, ci), _ = routes(kind, n_max, B, n_local, keep_first)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o2, l2 = bsa.decode(q.cuda(), k.cuda(), v.cuda(), sl, rp, ci, B, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("kind", [R.BF1, R.SLIDING_WINDOW])
+def test_decode_routed_full_size(kind):
+    w = synth.WORKLOADS["qwen3_32k"]
+    q, k, v = make(1, w.heads_q, w.heads_kv, w.n, w.d, w.torch_dtype, seed=36)
+    rp, ci = R.route_csr(kind, w.n, w.block, n_local=w.n_local, keep_first=True)
+    for t in (w.n - 1, w.n // 2 + 77, 2 ** 14 - 1):
+        print(f"decode_routed qwen3_32k kind={kind} t={t}", flush=True)
+        o, lse = run_routed(q, k, v, [t + 1], kind, w.block, w.n_local)
+        ref, ref_lse = A.decode_attention(q, k, v, [t + 1], w.block, rp, ci, return_lse=True)
+        mx, rl2 = errors(o.float().cpu().numpy(), ref)
+        assert mx <= 1e-2 and rl2 <= 5e-3, (mx, rl2)
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-4
+
+
+def test_decode_routed_errors():
+    q = torch.zeros(1, 2, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 128, 64, dtype=torch.bfloat16, device="cuda")
+    sl = torch.ones(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(bsa.bsa_decode_workspace_bytes(1, 2, 64) // 4, dtype=torch.float32, device="cuda")
+    for spec, status in ((bsa.route_spec(R.STATIC_RANDOM), bsa.BSA_ERR_UNSUPPORTED),
+                         (bsa.route_spec(7), bsa.BSA_ERR_INVALID_ARGUMENT),
+                         (bsa.route_spec(R.BF1, n_local=-1), bsa.BSA_ERR_INVALID_ARGUMENT)):
+        with pytest.raises(bsa.BsaError) as e:
+            bsa.bsa_decode_routed(q, k, k, torch.empty_like(q), sl, spec, 64, ws)
+        assert e.value.status == status
+    with pytest.raises(bsa.BsaError) as e:
+        bsa.bsa_decode_routed(q, k, k, torch.empty_like(q), sl, bsa.route_spec(R.BF1), 64, ws[:8])
+    assert e.value.status == bsa.BSA_ERR_CAPACITY

@@ -16,6 +16,7 @@ import long_context_block_amd as bsa
 from oracle import attn as A
 from oracle import routes as R
 import synth
+from route_ref import workload_routes
 
 pytestmark = pytest.mark.gpu
 
@@ -34,19 +35,17 @@ def errors(got, ref):
 
 
 def route_for(w, kind=None):
-    kind = w.route_kind if kind is None else kind
-    spec = bsa.route_spec(kind, w.n_local, w.keep_first, w.n_random, w.route_seed)
-    return bsa.build_route(spec, w.n, w.block)
+    return workload_routes(w, kind)[0]
 
 
 def run_gpu(w, q, k, v, kind=None, with_lse=False, stream=None):
-    rp, ci = route_for(w, kind)
+    (rp, ci), oracle_rc = workload_routes(w, kind)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = bsa.forward(qd, kd, vd, rp, ci, w.block, with_lse=with_lse, stream=stream)
     torch.cuda.synchronize()
     if not with_lse:
         out = (out, None)
-    return out, (rp.cpu().numpy(), ci.cpu().numpy())
+    return out, oracle_rc
 
 
 def sample_rows(n, B, rng, extra=24):
@@ -241,10 +240,10 @@ def test_dense_causal_ref_equals_forward_on_dense_route():
 def test_explicit_scale():
     w = synth.WORKLOADS["bf1_4k"].resized(n=600, heads_q=2, heads_kv=2)
     q, k, v = synth.make_qkv(w)
-    rp, ci = route_for(w)
+    (rp, ci), (orp, oci) = workload_routes(w)
     o = bsa.forward(q.cuda(), k.cuda(), v.cuda(), rp, ci, w.block, scale=0.05)
     torch.cuda.synchronize()
-    ref = A.attention(q, k, v, w.block, rp.cpu().numpy(), ci.cpu().numpy(), scale=0.05)
+    ref = A.attention(q, k, v, w.block, orp, oci, scale=0.05)
     mx, rl2 = errors(o.float().cpu().numpy(), ref)
     assert mx <= BF16_MAXABS and rl2 <= BF16_RELL2
 
