@@ -180,7 +180,7 @@ size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block);
  * blocks, the segment table of the transposed rows, and fp32
  * partial dk/dv of key blocks whose readers are split over several work-groups); its contents
  * on entry do not matter.  Supported: dtype BF16; d in {64, 128}; block in {64, 128}; any n >= 0.
- * Five kernels on `stream`; the result is deterministic (no atomics).
+ * Four kernels on `stream`; the result is deterministic (no atomics).
  */
 bsa_status bsa_backward(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                         const float* lse, void* dq, void* dk, void* dv, int32_t batch, int32_t heads_q,

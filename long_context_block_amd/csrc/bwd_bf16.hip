@@ -9,10 +9,10 @@
 // K and the forward's log-sum-exp; excluded pairs have P = 0 and carry no gradient.
 //
 // How (gfx950; the structure of the unpipelined forward kernel, run twice):
-//  * bwd_prep_kernel: D[t] = sum_d dO[t, d] O[t, d] in fp32, one 16-byte slice per lane.
 //  * bwd_dq_kernel: one work-group per (batch, query head, query block i), 32 query rows per
-//    wavefront, walking row i of the route in 64-key chunks copied HBM -> LDS one chunk ahead
-//    (global_load_lds_dwordx4, two stages).  Per chunk, on the matrix cores: S^T = K Q^T and
+//    wavefront.  It first forms D[t] = sum_d dO[t, d] O[t, d] for its rows on the matrix cores
+//    (and writes D and lse log2(e) for the dK/dV kernel), then walks row i of the route in 64-key chunks
+//    copied HBM -> LDS one chunk ahead (global_load_lds_dwordx4, two stages).  Per chunk, on the matrix cores: S^T = K Q^T and
 //    dP^T = V dO^T (K, V rows from LDS; Q, dO resident in registers), then dS^T = P^T (dP^T - D)
 //    in registers (one query per lane), then dQ^T += K^T dS^T with K^T read transposed by the
 //    LDS unit (ds_read_b64_tr_b16).
@@ -26,37 +26,6 @@ namespace bsa {
 namespace {
 
 using namespace bwd;
-
-// ---- D = rowsum(dO * O), lse * log2(e) -----------------------------------------------------------
-// Both over rows padded to whole blocks: past n, D = 0 and lse2 = +inf, so that a padded query
-// row has P = exp2(s - lse2) = 0 without a mask.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-    constexpr int LPR = D / 8;  // lanes per row (16 bytes each)
-    const int64_t prow = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;  // padded row
-    const int c = threadIdx.x % LPR;
-    const int64_t bh = prow / p.n_pad, t = prow % p.n_pad;
-    const bool in = bh < (int64_t)p.batch * p.heads_q;
-    const int64_t row = bh * p.n + t;
-    float s = 0.f;
-    if (in && t < p.n) {
-        const uint4 a = *(const uint4*)((const __bf16*)p.d_o + row * D + c * 8);
-        const uint4 o = *(const uint4*)((const __bf16*)p.o + row * D + c * 8);
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, ow[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            s = fmaf(__uint_as_float(aw[x] << 16), __uint_as_float(ow[x] << 16), s);
-            s = fmaf(__uint_as_float(aw[x] & 0xffff0000u), __uint_as_float(ow[x] & 0xffff0000u), s);
-        }
-    }
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) s += __shfl_xor(s, o);
-    if (in && c == 0) {
-        p.dvec[prow] = s;
-        p.lse2[prow] = t < p.n ? p.lse[row] * kLog2e : __builtin_inff();
-    }
-    if (blockIdx.x == 0 && threadIdx.x < 64) p.ld_pad[threadIdx.x] = threadIdx.x < 32 ? __builtin_inff() : 0.f;
-}
 
 // ---- dQ --------------------------------------------------------------------------------------
 template <int D, int BLK>
@@ -92,8 +61,37 @@ void bwd_dq_kernel(BwdParams p) {
             dof[kk] = row_ok ? *(const bf16x8*)(Gr + 16 * kk + 8 * hf) : bf16x8{};
         }
     }
+    // D = rowsum(dO * O) of this lane's row, as the diagonal of the 32 x 32 product O dO^T of
+    // the wavefront's rows, formed on the matrix cores with the operand layout and order of
+    // dP^T = V dO^T below: where the mathematics makes dP - D vanish (a row whose only selected
+    // key is its own token, O = V) it vanishes exactly.  D and lse * log2(e) are also written for
+    // the dK/dV kernel, over rows padded to whole blocks (past n: D = 0 and lse2 = +inf, so that a
+    // padded query row has P = exp2(s - lse2) = 0 without a mask); this work-group's rows are
+    // exactly its block's.
+    float dval;
+    {
+        const __bf16* Or = (const __bf16*)p.o + (bh * n + (row_ok ? qrow : 0)) * D;
+        f32x16 x = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const bf16x8 of = row_ok ? *(const bf16x8*)(Or + 16 * kk + 8 * hf) : bf16x8{};
+            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, dof[kk], x, 0, 0, 0);
+        }
+        // lane l holds column l32 at rows 8 (r / 4) + 4 hf + r % 4: the diagonal entry of column
+        // l32 is in the half-wavefront hf = (l32 / 4) % 2, at r = 4 (l32 / 8) + l32 % 4
+        const int rd = 4 * (l32 >> 3) + (l32 & 3);
+        float mine = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine = (r == rd) ? x[r] : mine;
+        const float other = __shfl_xor(mine, 32);
+        dval = (hf == ((l32 >> 2) & 1)) ? mine : other;
+    }
     const float lse2 = row_ok ? p.lse[bh * n + qrow] * kLog2e : 0.f;
-    const float dval = row_ok ? p.dvec[bh * p.n_pad + qrow] : 0.f;
+    if (hf == 0) {
+        p.dvec[bh * p.n_pad + i * BLK + qloc] = dval;
+        p.lse2[bh * p.n_pad + i * BLK + qloc] = row_ok ? lse2 : __builtin_inff();
+    }
+    if (blockIdx.x == 0 && tid < 64) p.ld_pad[tid] = tid < 32 ? __builtin_inff() : 0.f;
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -231,13 +229,9 @@ __global__ __launch_bounds__(1024) void bwd_seg_kernel(BwdParams p, int cpb) {
 
 template <int D, int BLK>
 hipError_t launch_t(const BwdParams& p, hipStream_t stream) {
-    const int64_t rows = (int64_t)p.batch * p.heads_q * p.n_pad;
-    const int64_t prep_blocks = (rows * (D / 8) + 255) / 256;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_seg_kernel, dim3(1), dim3(1024), 0, stream, p, BLK / kCh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_seg_kernel, dim3(1), dim3(1024), 0, stream, p, BLK / kCh);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, BLK>), dim3((unsigned)((int64_t)p.batch * p.heads_q * p.nqb)),
                        dim3(BLK / 32 * 64), 0, stream, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -5,7 +5,7 @@
 //     dV[t'] = sum over (query head h of g, query t with (t, t') selected) of P[t, t'] dO[t],
 //     dK[t'] = scale * the same sum of dS[t, t'] Q[t],   dS = P (dP - D),  dP = dO V^T,
 // where P = exp(scale q.k - lse) is recomputed from the forward's log-sum-exp, D = rowsum(dO * O)
-// (bwd_prep_kernel), and a pair takes part when the route selects block (i, j) and, on the
+// (written by bwd_dq_kernel), and a pair takes part when the route selects block (i, j) and, on the
 // diagonal block, the query does not precede the key ("Block-Sparse Attention", "Math Or Compute
 // Schema").  The sums over t run over the transposed route: the query blocks i whose rows hold j.
 //
