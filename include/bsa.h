@@ -260,9 +260,10 @@ bsa_status bsa_decode_routed(const void* q, const void* k_cache, const void* v_c
  * Inputs (device, caller-owned, contiguous, 16-byte aligned, bf16): q [batch, heads_q, n, d];
  * k, v [batch, heads_kv, n, d]; r_meta (meta queries) [batch, heads_q, nch, d]; h_meta (meta
  * keys) [batch, heads_kv, nch, d].  Output o like q.  scale <= 0 selects 1/sqrt(d) for both
- * softmaxes.  workspace: at least bsa_bsbr_workspace_bytes(...) bytes (fp32 chunk states, meta
- * weights and retrieved states); contents on entry do not matter.  Supported: BF16; d in
- * {64, 128}; chunk in {64, 128}; 1 <= nch <= 1024.  Four kernels on `stream`, no atomics.
+ * softmaxes.  workspace: at least bsa_bsbr_workspace_bytes(...) bytes (fp32 chunk states per
+ * key/value head and retrieved states per query head); contents on entry do not matter.
+ * Supported: BF16; d in {64, 128}; chunk in {64, 128}; 1 <= nch <= 1024.  Three kernels on
+ * `stream`, no atomics.
  * Errors: BSA_ERR_INVALID_ARGUMENT (NULL or misaligned pointers, bad sizes), BSA_ERR_UNSUPPORTED
  * (dtype, d, chunk, nch), BSA_ERR_CAPACITY (workspace), BSA_ERR_DEVICE (launch failure).
  */

@@ -392,7 +392,6 @@ size_t bsa_bsbr_workspace_bytes(int32_t batch, int32_t heads_q, int32_t heads_kv
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv || n < 1 || d < 1 || chunk < 1) return 0;
     const size_t nch = (size_t)((n + chunk - 1) / chunk);
     return align256((size_t)batch * heads_kv * nch * d * d * sizeof(float)) +
-           align256((size_t)batch * heads_q * nch * nch * sizeof(float) + 64) +
            (size_t)batch * heads_q * nch * d * d * sizeof(float);
 }
 
@@ -428,8 +427,6 @@ bsa_status bsa_bsbr_forward(const void* q, const void* k, const void* v, const v
     p.q = q; p.k = k; p.v = v; p.r = r_meta; p.h = h_meta; p.o = o;
     p.F = (float*)ws;
     ws += align256((size_t)batch * heads_kv * nch * d * d * sizeof(float));
-    p.W = (float*)ws;
-    ws += align256((size_t)batch * heads_q * nch * nch * sizeof(float) + 64);
     p.A = (float*)ws;
     p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.nch = (int32_t)nch; p.n = n;
     const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);

@@ -155,7 +155,6 @@ struct BsbrParams {
     const void* h;    // meta keys [batch, heads_kv, nch, d]
     void* o;          // [batch, heads_q, n, d]
     float* F;         // workspace: chunk states [batch, heads_kv, nch, d * d] (32 x 32 tiles)
-    float* W;         // workspace: meta weights [batch, heads_q, nch, nch]
     float* A;         // workspace: retrieved states [batch, heads_q, nch, d * d]
     int32_t batch, heads_q, heads_kv, nch;
     int64_t n;

@@ -10,18 +10,16 @@
 // R (meta queries, per query head) and H (meta keys, per key/value head) are inputs, one d-vector
 // per chunk.
 //
-// How (gfx950; four kernels, every input read once, intermediates in fp32):
+// How (gfx950; three kernels, every input read once, intermediates in fp32):
 //  * bsbr_state_kernel: one work-group per (batch, kv head, chunk).  K and V of the chunk go to
 //    LDS (rows past n zero-filled); F = K^T V on the matrix cores (bf16 products are exact in the
 //    fp32 accumulator), both operands read transposed by the LDS unit (ds_read_b64_tr_b16).  F is
 //    stored as 32 x 32 fp32 tiles in the accumulator's order: element (i, j) of tile
 //    (i / 32, j / 32) sits at [(tile * 32 + j % 32) * 32 + i % 32], tile = (i / 32) * d / 32 + j / 32.
-//  * bsbr_meta_kernel: one wavefront per (batch, query head, chunk): dot products of R_c with the
-//    earlier H rows, max and sum across the wavefront, and the row of W stored transposed.
-//  * bsbr_mix_kernel: A = W F as a small fp32 GEMM per (batch, query head) over the flattened
-//    d*d states (layout-agnostic): a work-group takes 16 chunks x 64 state elements, its four
-//    wavefronts split the earlier chunks and their partials are summed in LDS in a fixed order;
-//    the group's weights are staged in LDS with one coalesced pass.
+//  * bsbr_mix_kernel: per (batch, query head, 32 chunks, 128 of the flattened d*d state
+//    elements): the meta scores of the 32 chunks against the earlier ones on the matrix cores,
+//    their softmax in LDS, then A = W F with the fp32 matrix-core product (F rows read once per
+//    32-chunk tile, coalesced).
 //  * bsbr_chunk_kernel: one work-group per (batch, query head, chunk), one wavefront per 32
 //    queries: the within-chunk attention (exact softmax over the chunk's keys) and the retrieval
 //    read-out on the matrix cores, with A_c split into two bf16 parts, and one output store.
@@ -82,125 +80,153 @@ __global__ __launch_bounds__(256) void bsbr_state_kernel(BsbrParams p) {
     }
 }
 
+constexpr int kMixE = 128;  // flattened state elements per work-group: 4 wavefronts x 32
+constexpr int kMixKB = 64;  // earlier chunks per block of the A = W F product
+
+// Position of earlier chunk c' in an LDS row of weights: within each block of 64, the even
+// chunks first, then the odd ones, so that a lane's operands of one block (chunks k0 + 2 y + hf,
+// y = 0..31) are 32 consecutive floats.
+__device__ inline int mix_pos(int cp) { return (cp & ~63) + ((cp & 1) << 5) + ((cp & 63) >> 1); }
+
+// The retrieved states of 32 consecutive chunks c0 .. c0 + 31 for one (batch, query head), over
+// 128 of the d*d state elements (the sum is layout-agnostic over them):
+//  1. meta scores S[i][c'] = scale R_{c0+i} . H_c' for every c' the tile's rows can see, on the
+//     matrix cores (bf16 products are exact in the fp32 accumulator); wavefront w takes the
+//     32-chunk column blocks w, w + 4, ...; the scores go to LDS rows (stride 4 mod 64 floats, so
+//     that the 16-byte operand reads of step 3 are conflict-free);
+//  2. the softmax numerators exp2(S - max) over c' < c0 + i in place (zero elsewhere) and the
+//     row's 1 / sum (8 threads per row, 8 weights per LDS batch; row 0 of chunk 0 has no earlier
+//     chunk and stays all zero);
+//  3. A[c0 + i][e] = (1 / sum_i) sum over c' of exp[i][c'] F[c'][e] with the fp32 matrix-core
+//     product v_mfma_f32_32x32x2_f32 (A operand: the numerators from LDS, B operand: F rows read
+//     straight from global memory, 32 consecutive elements per half-wavefront, in blocks of 64
+//     earlier chunks; the first block is requested at entry, so that its latency overlaps steps 1
+//     and 2); two accumulators; wavefront w owns elements 32 w .. 32 w + 31 of the slice.
+// Each work-group recomputes its 32 rows of meta scores (a few matrix-core instructions), so no
+// weight matrix is stored.
 template <int D>
-__global__ __launch_bounds__(64) void bsbr_meta_kernel(BsbrParams p) {
-    const int lane = threadIdx.x;
-    const int64_t w = blockIdx.x;  // (b * heads_q + h) * nch + c
+__global__ __launch_bounds__(256) void bsbr_mix_kernel(BsbrParams p) {
+    extern __shared__ __attribute__((aligned(16))) float sW[];  // [32][ldw], then 1 / sum [32]
+    constexpr int DD = D * D;
+    constexpr int slices = DD / kMixE;
     const int nch = p.nch;
-    const int c = (int)(w % nch);
-    const int64_t bh = w / nch, b = bh / p.heads_q, h = bh % p.heads_q;
-    const int G = p.heads_q / p.heads_kv;
-    const __bf16* Rc = (const __bf16*)p.r + w * D;
-    const __bf16* Hg = (const __bf16*)p.h + (b * p.heads_kv + h / G) * (int64_t)nch * D;
-    float rv[D];
-#pragma unroll
-    for (int x = 0; x < D / 8; ++x) {
-        const uint4 u = *(const uint4*)(Rc + 8 * x);
-        const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            rv[8 * x + 2 * y] = __uint_as_float(wds[y] << 16);
-            rv[8 * x + 2 * y + 1] = __uint_as_float(wds[y] & 0xffff0000u);
-        }
-    }
-    auto score = [&](int cp) {  // scale * R_c . H_cp, log2 units
-        const __bf16* Hr = Hg + (int64_t)cp * D;
-        float s = 0.f;
-#pragma unroll
-        for (int x = 0; x < D / 8; ++x) {
-            const uint4 u = *(const uint4*)(Hr + 8 * x);
-            const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                s = fmaf(rv[8 * x + 2 * y], __uint_as_float(wds[y] << 16), s);
-                s = fmaf(rv[8 * x + 2 * y + 1], __uint_as_float(wds[y] & 0xffff0000u), s);
-            }
-        }
-        return s * p.scale_log2;
-    };
-    float mx = -INFINITY;
-    for (int cp = lane; cp < c; cp += 64) mx = fmaxf(mx, score(cp));
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float sum = 0.f;
-    for (int cp = lane; cp < c; cp += 64) sum += __builtin_amdgcn_exp2f(score(cp) - mx);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-    const float inv = c > 0 ? 1.f / sum : 0.f;
-    // stored transposed, W^T[c'][c], so that the mix reads the weights of consecutive chunks c
-    // for one earlier chunk c' as one scalar load
-    float* Wt = p.W + bh * nch * (int64_t)nch + c;
-    for (int cp = lane; cp < nch; cp += 64)
-        Wt[(int64_t)cp * nch] = cp < c ? __builtin_amdgcn_exp2f(score(cp) - mx) * inv : 0.f;
-}
-
-constexpr int kMixRows = 16;   // chunks per work-group (accumulators per thread)
-constexpr int kMixCols = 64;   // state elements per work-group (one per lane)
-constexpr int kMixPf = 8;      // earlier chunks per wavefront step (their loads issued together)
-
-// A[c][e] = sum over c' < c of W[c][c'] F[c'][e].  Work-group = 16 chunks c x 64 state elements e;
-// its 4 wavefronts split the earlier chunks c' (wavefront w takes c' = w mod 4) so that each
-// lane's chain of dependent loads is a quarter as long, and sum their partials in LDS in a fixed
-// order.  The group's weights (16 per earlier chunk, contiguous in W^T) are staged in LDS once
-// and read back as broadcasts.
-__global__ __launch_bounds__(256) void bsbr_mix_kernel(BsbrParams p, int dd) {
-    __shared__ float part[4][kMixRows][kMixCols];
-    extern __shared__ __attribute__((aligned(16))) float sWt[];  // [c' < cmax][16]
-    const int nch = p.nch;
-    const int slices = dd / kMixCols;
-    const int groups = (nch + kMixRows - 1) / kMixRows;
+    const int ldw = ((nch + 63) & ~63) + 4;
+    float* sInv = sW + 32 * ldw;
+    const int tiles = (nch + 31) / 32;
     const int64_t w = blockIdx.x;
     const int slice = (int)(w % slices);
-    const int grp = (int)((w / slices) % groups);
-    const int64_t bh = w / slices / groups;
+    const int ct = (int)((w / slices) % tiles);
+    const int64_t bh = w / slices / tiles;
     const int64_t b = bh / p.heads_q, h = bh % p.heads_q;
-    const int G = p.heads_q / p.heads_kv;
-    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c0 = grp * kMixRows;
-    const int rows = (nch - c0) < kMixRows ? nch - c0 : kMixRows;
-    const int cmax = c0 + rows - 1;  // the group's last chunk reads chunks c' < cmax
-    const int e = slice * kMixCols + lane;
-    const float* Fg = p.F + (b * p.heads_kv + h / G) * (int64_t)nch * dd + e;
-    // W^T row c' for this group: Wt[c' * nch + c0 .. + 16].  All 16 are read even when the group
-    // has fewer chunks (the workspace pads W by 16 floats); the extra rows are never stored.
-    const float* Wt = p.W + bh * nch * (int64_t)nch + c0;
-    for (int x = threadIdx.x; x < cmax * kMixRows; x += 256)
-        sWt[x] = Wt[(int64_t)(x / kMixRows) * nch + x % kMixRows];
-    __syncthreads();
-    float acc[kMixRows];
+    const int64_t bg = b * p.heads_kv + h / (p.heads_q / p.heads_kv);
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = 32 * ct;
+    const int rows = (nch - c0) < 32 ? nch - c0 : 32;
+    const int ncp = c0 + rows - 1;  // the tile's rows see the chunks c' < ncp
+    const int ncp64 = (ncp + 63) & ~63;
+
+    // F values of one block: chunk k0 + 2 y + hf, element e (zero past ncp)
+    const int e = slice * kMixE + 32 * wv + l32;
+    const float* Fg = p.F + bg * nch * (int64_t)DD + e;
+    float f[kMixKB / 2];
+    auto load_block = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < kMixRows; ++u) acc[u] = 0.f;
-    for (int cb = wv; cb < cmax; cb += 4 * kMixPf) {
-        float f[kMixPf];
-#pragma unroll
-        for (int y = 0; y < kMixPf; ++y) {
-            const int cp = cb + 4 * y;
-            f[y] = cp < cmax ? Fg[(int64_t)cp * dd] : 0.f;
+        for (int y = 0; y < kMixKB / 2; ++y) {
+            const int cp = k0 + 2 * y + hf;
+            f[y] = cp < ncp ? Fg[(int64_t)cp * DD] : 0.f;
         }
+    };
+    load_block(0);
+
+    // 1. meta scores of the tile's rows against chunks c' < ncp64 (zero past ncp)
+    {
+        const int rc = c0 + l32;
+        const __bf16* Rr = (const __bf16*)p.r + (bh * nch + (l32 < rows ? rc : c0)) * D;
+        bf16x8 rf[D / 16];
 #pragma unroll
-        for (int y = 0; y < kMixPf; ++y) {
-            const int cp = cb + 4 * y;
-            if (cp >= cmax) break;
-            const float4* wr = (const float4*)(sWt + cp * kMixRows);
+        for (int kk = 0; kk < D / 16; ++kk) rf[kk] = l32 < rows ? *(const bf16x8*)(Rr + 16 * kk + 8 * hf) : bf16x8{};
+        const __bf16* Hg = (const __bf16*)p.h + bg * nch * (int64_t)D;
+        for (int cb = wv; 32 * cb < ncp64; cb += 4) {
+            const int cp = 32 * cb + l32;  // this lane's column c'
+            const __bf16* Hr = Hg + (int64_t)(cp < ncp ? cp : 0) * D;
+            f32x16 acc = f32x16{};
 #pragma unroll
-            for (int q4 = 0; q4 < kMixRows / 4; ++q4) {
-                const float4 wq = wr[q4];
-                acc[4 * q4] = fmaf(wq.x, f[y], acc[4 * q4]);
-                acc[4 * q4 + 1] = fmaf(wq.y, f[y], acc[4 * q4 + 1]);
-                acc[4 * q4 + 2] = fmaf(wq.z, f[y], acc[4 * q4 + 2]);
-                acc[4 * q4 + 3] = fmaf(wq.w, f[y], acc[4 * q4 + 3]);
+            for (int kk = 0; kk < D / 16; ++kk) {
+                const bf16x8 hv = cp < ncp ? *(const bf16x8*)(Hr + 16 * kk + 8 * hf) : bf16x8{};
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[kk], hv, acc, 0, 0, 0);
             }
+            // lane holds column cp at rows 8 (r / 4) + 4 hf + r % 4
+            const int pc = mix_pos(cp);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sW[(8 * (r >> 2) + 4 * hf + (r & 3)) * ldw + pc] = acc[r] * p.scale_log2;
         }
     }
-#pragma unroll
-    for (int u = 0; u < kMixRows; ++u) part[wv][u][lane] = acc[u];
     __syncthreads();
-    // wavefront w sums rows u = 4 w .. 4 w + 3 over the four partials, in order
-    float* Ao = p.A + (bh * nch + c0) * (int64_t)dd + e;
+    // 2. numerators exp2(S - max) for c' < c0 + i, zero for the other positions < ncp64; 1 / sum.
+    //    Thread (i, part) takes positions 8 part + 64 m + (0..7), m = 0, 1, ... (two float4s).
+    {
+        const int i = tid >> 3, part = tid & 7;
+        const int len = i < rows ? c0 + i : 0;
+        float* row = sW + i * ldw;
+        auto chunk_of = [](int pos) { return (pos & ~63) + 2 * (pos & 31) + ((pos >> 5) & 1); };
+        float mx = -INFINITY;
+        for (int p0 = 8 * part; p0 < ncp64; p0 += 64) {
+            const float4 a = *(const float4*)(row + p0), z = *(const float4*)(row + p0 + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, z.x, z.y, z.z, z.w};
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-        const int u = 4 * wv + y;
-        if (u < rows) Ao[(int64_t)u * dd] = ((part[0][u][lane] + part[1][u][lane]) + part[2][u][lane]) + part[3][u][lane];
+            for (int u = 0; u < 8; ++u)
+                if (chunk_of(p0 + u) < len) mx = fmaxf(mx, v[u]);
+        }
+        // max and sum over the row's 8 consecutive lanes by DPP (no LDS round trips)
+        mx = fmaxf(mx, lanes::xor_lane<1>(mx));
+        mx = fmaxf(mx, lanes::xor_lane<2>(mx));
+        mx = fmaxf(mx, lanes::half_mirror(mx));
+        float sum = 0.f;
+        for (int p0 = 8 * part; p0 < ncp64; p0 += 64) {
+            const float4 a = *(const float4*)(row + p0), z = *(const float4*)(row + p0 + 4);
+            const float v[8] = {a.x, a.y, a.z, a.w, z.x, z.y, z.z, z.w};
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                x[u] = chunk_of(p0 + u) < len ? __builtin_amdgcn_exp2f(v[u] - mx) : 0.f;
+                sum += x[u];
+            }
+            *(float4*)(row + p0) = make_float4(x[0], x[1], x[2], x[3]);
+            *(float4*)(row + p0 + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        }
+        sum = lanes::group_sum<8>(sum);
+        if (part == 0) sInv[i] = len > 0 ? 1.f / sum : 0.f;
+    }
+    __syncthreads();
+    // 3. A = (1 / sum) exp F over c' < ncp, two earlier chunks per instruction (k = hf)
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+    const float* Wr = sW + l32 * ldw + 32 * hf;
+    for (int k0 = 0;;) {
+        float wa[kMixKB / 2];
+#pragma unroll
+        for (int y4 = 0; y4 < kMixKB / 8; ++y4) {
+            const float4 t = *(const float4*)(Wr + k0 + 4 * y4);
+            wa[4 * y4] = t.x;
+            wa[4 * y4 + 1] = t.y;
+            wa[4 * y4 + 2] = t.z;
+            wa[4 * y4 + 3] = t.w;
+        }
+#pragma unroll
+        for (int y = 0; y < kMixKB / 2; y += 2) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[y], f[y], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[y + 1], f[y + 1], acc1, 0, 0, 0);
+        }
+        k0 += kMixKB;
+        if (k0 >= ncp) break;
+        load_block(k0);
+    }
+    // lane holds element e at rows i = 8 (r / 4) + 4 hf + r % 4 of the tile
+    float* Ao = p.A + (bh * nch + c0) * (int64_t)DD + e;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (i < rows) Ao[(int64_t)i * DD] = (acc0[r] + acc1[r]) * sInv[i];
     }
 }
 
@@ -353,14 +379,17 @@ hipError_t launch_t(const BsbrParams& p, hipStream_t stream) {
                        stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bsbr_meta_kernel<D>), dim3((unsigned)q_chunks), dim3(64), 0, stream, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.nch > 1) {
-        const int dd = D * D, slices = dd / kMixCols, groups = (p.nch + kMixRows - 1) / kMixRows;
-        // dynamic LDS: the staged weights, at most 16 x (nch - 1) floats (<= 64 KiB at 1024 chunks)
-        const size_t lds = (size_t)kMixRows * (p.nch - 1) * sizeof(float);
-        hipLaunchKernelGGL(bsbr_mix_kernel, dim3((unsigned)((int64_t)p.batch * p.heads_q * groups * slices)),
-                           dim3(256), lds, stream, p, dd);
+        // dynamic LDS: the meta scores / weights of 32 chunks, 32 rows of (nch rounded up to 64)
+        // + 4 floats, and 32 row factors (about 129 KiB at 1024 chunks)
+        const size_t lds = ((size_t)32 * (((p.nch + 63) & ~63) + 4) + 32) * sizeof(float);
+        if (lds > 65536 &&
+            (e = hipFuncSetAttribute((const void*)bsbr_mix_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds)) != hipSuccess)
+            return e;
+        const int64_t tiles = (p.nch + 31) / 32;
+        hipLaunchKernelGGL((bsbr_mix_kernel<D>), dim3((unsigned)((int64_t)p.batch * p.heads_q * tiles * (D * D / kMixE))),
+                           dim3(256), lds, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     hipLaunchKernelGGL((bsbr_chunk_kernel<D, BLK>), dim3((unsigned)q_chunks), dim3(BLK / 32 * 64), 0, stream, p);

@@ -194,10 +194,10 @@ def test_bsbr_rejects_bad_arguments(kw, status):
 
 
 def test_bsbr_workspace_and_empty_batch():
-    # fp32 states per kv head, meta weights (+ 16 floats) and retrieved states per query head
+    # fp32 states per kv head and retrieved states per query head
     nch, d, hq, hkv = 8, 64, 3, 1
     align = lambda x: -(-x // 256) * 256  # noqa: E731
-    want = align(hkv * nch * d * d * 4) + align(hq * nch * nch * 4 + 64) + hq * nch * d * d * 4
+    want = align(hkv * nch * d * d * 4) + hq * nch * d * d * 4
     assert bsa.bsa_bsbr_workspace_bytes(1, 3, 1, 1000, 64, 128) == want
     assert bsa.bsa_bsbr_workspace_bytes(1, 3, 2, 1000, 64, 128) == 0
     assert _raw_bsbr(batch=0, q=None, k=None, v=None, r=None, h=None, o=None, ws=None) == bsa.BSA_OK

@@ -85,6 +85,22 @@ def test_bsbr_full_size_sampled_rows():
     assert rl2 <= RELL2 and mx <= MAXREL, (rl2, mx)
 
 
+@pytest.mark.parametrize("w,rows", [
+    # 1024 chunks of 64 (the largest count): the meta weights of a 32-chunk tile span 1024 chunks
+    (C3.resized(name="c1024-d64-c64", n=65536, block=64, heads_q=1, heads_kv=1, batch=1),
+     [0, 63, 64, 2047, 2048, 2049, 33000, 65471, 65472, 65535]),
+    # 100 chunks, the last one partial and the last 32-chunk tile short; GQA at d = 128
+    (C3.resized(name="c100-gqa2-d128-c64", n=6370, block=64, d=128, heads_q=4, heads_kv=2, batch=1),
+     [0, 64, 2047, 2048, 4000, 6143, 6335, 6336, 6369]),
+])
+def test_bsbr_many_chunks_sampled_rows(w, rows):
+    print(f"bsbr {w.name}", flush=True)
+    got, ref, _ = run(w, rows=np.array(rows))
+    rl2, mx = errors(got, ref)
+    print(f"  rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)
+    assert rl2 <= RELL2 and mx <= MAXREL, (rl2, mx)
+
+
 def test_bsbr_deterministic():
     w = C3.resized(n=2000, batch=1)
     q, k, v = (x.cuda() for x in synth.make_qkv(w))
