@@ -238,12 +238,11 @@ __global__ __launch_bounds__(256) void bsbr_mix_kernel(BsbrParams p) {
 //   transposed; then O^T += A_c^T Q^T on the matrix cores with A_c split into bf16 hi and lo
 //   parts (the same Q fragments are the B operand), and one bf16 store.
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK / 32 * 64) void bsbr_chunk_kernel(BsbrParams p) {
+__global__ __launch_bounds__(BLK / 32 * 64) __attribute__((amdgpu_waves_per_eu(4))) void bsbr_chunk_kernel(BsbrParams p) {
     constexpr int NW = BLK / 32;
     constexpr int NT = D / 32;
     __shared__ __attribute__((aligned(1024))) __bf16 sK[BLK * D];
     __shared__ __attribute__((aligned(1024))) __bf16 sV[BLK * D];
-    __shared__ __attribute__((aligned(16))) float sA[D * D];  // A_c in the tile layout
     const int nch = p.nch;
     const int64_t w = blockIdx.x;  // (b * heads_q + h) * nch + c
     const int c = (int)(w % nch);
@@ -263,10 +262,6 @@ __global__ __launch_bounds__(BLK / 32 * 64) void bsbr_chunk_kernel(BsbrParams p)
             const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
             *(uint4*)(sK + Sw2<D>::off(r, cc)) = r < rows ? *(const uint4*)(K + (int64_t)r * D + cc * 8) : zero;
             *(uint4*)(sV + Sw2<D>::off(r, cc)) = r < rows ? *(const uint4*)(V + (int64_t)r * D + cc * 8) : zero;
-        }
-        if (c > 0) {
-            const float* Ac = p.A + w * (int64_t)(D * D);
-            for (int x = tid; x < D * D / 4; x += NW * 64) *(float4*)(sA + 4 * x) = *(const float4*)(Ac + 4 * x);
         }
     }
     const int qloc = 32 * wv + l32;  // this lane's query within the chunk
@@ -341,13 +336,16 @@ __global__ __launch_bounds__(BLK / 32 * 64) void bsbr_chunk_kernel(BsbrParams p)
         for (int r = 0; r < 16; ++r) acc[db][r] *= inv;
     // retrieval: O^T[j][query] += sum_i A_c[i][j] Q[query][i]
     if (c > 0) {
+        // A_c read straight from global memory (the four wavefronts share it through the caches),
+        // so that LDS holds only K_c and V_c and four work-groups fit a CU
+        const float* Ac = p.A + w * (int64_t)(D * D);
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const int i0 = 16 * ks + 8 * hf;  // this lane's 8 values of i
 #pragma unroll
             for (int nb = 0; nb < NT; ++nb) {
                 // A_c^T row j = 32 nb + l32, i = i0 .. i0 + 7: tile (i / 32, j / 32), offset j % 32, i % 32
-                const float* src = sA + ((i0 / 32) * NT + nb) * 1024 + l32 * 32 + (i0 % 32);
+                const float* src = Ac + ((i0 / 32) * NT + nb) * 1024 + l32 * 32 + (i0 % 32);
                 const float4 a0 = *(const float4*)src, a1 = *(const float4*)(src + 4);
                 const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                 bf16x8 ahi, alo;
