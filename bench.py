@@ -143,10 +143,11 @@ def graph_depth(row_ptr: np.ndarray, col_idx: np.ndarray) -> tuple[int, int]:
 
 
 def topology_sweep(w, qd, kd, vd, steps: int) -> dict:
-    """BF1 against its two equal-budget controls on the same inputs ("BF1 ...", section 5
-    "Topology control": equal-pair-count BF1, sliding and static-random routes have nearly
-    identical sparse kernel time; "Communication depth"): the local sliding band and the
-    static-random graph whose parameter gives the selected-pair count nearest to BF1's."""
+    """BF1 against its two equal-budget controls on the same inputs ("BF1 ...", section 5,
+    "Topology control" and "Communication depth": at a matched pair count the page finds the three
+    topologies' sparse kernel times close together, and compares their depths): the local sliding
+    band and the static-random graph whose parameter gives the selected-pair count nearest to
+    BF1's."""
     import torch
     import long_context_block_amd as bsa
     od = torch.empty_like(qd)

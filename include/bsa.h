@@ -113,7 +113,10 @@ bsa_status bsa_build_route(const bsa_route_spec* spec, int64_t n, int32_t block,
  * the first entry is j itself).  The gradients of K and V walk these rows (bsa_backward).
  * Input: a route accepted by bsa_check_route, nqb + 1 row pointers, nnz entries (device).
  * Output (device, caller-owned): t_row_ptr int32[nqb+1], t_col_idx int32[nnz] (a valid route
- * transposes to exactly nnz entries).  Integer kernels on `stream`; memory-safe on any input.
+ * transposes to exactly nnz entries).  Integer kernels on `stream`.  Memory-safe on any input:
+ * row pointers are read clamped to [0, nnz], every t_row_ptr value is clamped to nnz and no
+ * write goes past t_col_idx[nnz - 1], so a malformed route (say, overlapping rows) yields a
+ * meaningless but in-bounds transpose; results are defined only for valid routes.
  */
 bsa_status bsa_build_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
                                      int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream);

@@ -75,7 +75,13 @@ def check_m0(hipcc: str, src: str) -> None:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
     lines = [ln.strip() for ln in open(out)]
     for k, ln in enumerate(lines):
-        if ln.startswith(";") or "m0" not in ln.replace(",", " ").split():
+        if ln.startswith(";"):
+            continue
+        op = ln.split(" ", 1)[0]
+        # indexed register moves address registers through M0 without naming it
+        if op.startswith(("s_set_gpr_idx", "s_movrel", "v_movrel")):
+            raise RuntimeError(f"{src}: indexed register move (implicit M0 user) in generated code: {ln!r}")
+        if "m0" not in ln.replace(",", " ").split():
             continue
         nxt = lines[k + 1] if k + 1 < len(lines) else ""
         if not (ln.startswith("s_mov_b32 m0,") and nxt.startswith("global_load_lds_dword")):
@@ -89,17 +95,22 @@ def build(verbose: bool = False) -> str:
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(hipcc, s, verbose), srcs))
+    # every source, before anything is installed: the copy helpers reach some of them through
+    # headers, and a library whose code fails the check must never replace the previous one
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        list(ex.map(lambda s: check_m0(hipcc, s), srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    # every source: the copy helpers reach some of them through headers
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        list(ex.map(lambda s: check_m0(hipcc, s), srcs))
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, LIB)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
     return LIB
 
 

@@ -39,20 +39,11 @@ bsa_status device_error(hipError_t e, const char* where) {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-// Host-side nnz of a route (sum of closed-form row counts); -1 on overflow of int32.
+// Host-side nnz of a route: the closed-form start of the row past the last one (the same
+// function the route kernel writes row_ptr with); -1 if it does not fit int32.
 int64_t route_nnz(const bsa_route_spec& s, int64_t nqb) {
-    int64_t total = 0;
-    if (s.kind == BSA_ROUTE_DENSE_CAUSAL) {
-        total = nqb * (nqb + 1) / 2;
-    } else if (s.kind == BSA_ROUTE_BLOCK_DIAGONAL) {
-        total = nqb;
-    } else {
-        for (int64_t i = 0; i < nqb; ++i) {
-            total += bsa::route_row_count(s.kind, i, s.n_local, s.keep_first, s.n_random);
-            if (total > INT32_MAX) return -1;
-        }
-    }
-    return total > INT32_MAX ? -1 : total;
+    const int64_t total = bsa::route_row_start(s.kind, nqb, s.n_local, s.keep_first, s.n_random);
+    return (total < 0 || total > INT32_MAX) ? -1 : total;
 }
 
 bsa_status check_route_host(const int32_t* rp, const int32_t* ci, int64_t nqb, int64_t nnz) {

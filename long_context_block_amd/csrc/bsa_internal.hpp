@@ -9,7 +9,7 @@
 namespace bsa {
 
 // Closed-form |R(i)| for every route kind (see bsa_route_kind in bsa.h for the sets).
-// Used by the host (nnz, capacity checks) and by the device row-pointer kernel.
+// Used by the host (nnz, capacity checks) and by the device route kernels.
 __host__ __device__ inline int floor_log2_u64(uint64_t x) { return 63 - __builtin_clzll(x); }
 __host__ __device__ inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -37,6 +37,58 @@ __host__ __device__ inline int64_t route_row_count(int kind, int64_t i, int n_lo
     }
     case BSA_ROUTE_SLIDING_WINDOW:
         return 1 + (n_local < i ? n_local : i);
+    default:
+        return -1;
+    }
+}
+
+// Sum over k = 1 .. m of floor(log2 k) (0 for m <= 0): with K = floor(log2 m), the blocks
+// [2^j, 2^(j+1)) for j < K contribute j 2^j each, summing to (K - 2) 2^K + 2, and the partial
+// block [2^K, m] contributes K (m - 2^K + 1).
+__host__ __device__ inline int64_t sum_floor_log2(int64_t m) {
+    if (m <= 0) return 0;
+    const int K = floor_log2_u64((uint64_t)m);
+    const int64_t p = (int64_t)1 << K;
+    return (K - 2) * p + 2 + (int64_t)K * (m - p + 1);
+}
+
+// Sum over x = 0 .. N of min(cap, x) (0 for N < 0).
+__host__ __device__ inline int64_t sum_min_cap(int64_t N, int64_t cap) {
+    if (N < 0) return 0;
+    if (N <= cap) return N * (N + 1) / 2;
+    return cap * (cap + 1) / 2 + (N - cap) * cap;
+}
+
+// Closed-form start of row i in the CSR route: the sum of route_row_count over rows 0 .. i-1
+// (row_ptr[i]).  Lets one launch write every row without a scan.
+__host__ __device__ inline int64_t route_row_start(int kind, int64_t i, int n_local, int keep_first, int n_random) {
+    if (i <= 0) return 0;
+    const int64_t kf = keep_first ? 1 : 0;
+    switch (kind) {
+    case BSA_ROUTE_BF1: {
+        // rows r <= n_local hold 0 .. r (r + 1 entries); rows r > n_local hold the self block,
+        // n_local local blocks, the dyadic blocks with offset above n_local and, unless r is a
+        // power of two, block 0
+        const int64_t L = n_local;
+        const int64_t A = (i - 1 < L) ? i - 1 : L;  // rows 1 .. A lie inside the window
+        int64_t total = 1 + A + A * (A + 1) / 2;    // row 0, then rows 1 .. A
+        if (i - 1 > L) {
+            const int64_t cnt = i - 1 - L;          // rows L+1 .. i-1
+            const int64_t c = L >= 1 ? floor_log2_u64((uint64_t)L) + 1 : 0;  // dyadic offsets <= L
+            const int64_t pow2 = (floor_log2_u64((uint64_t)(i - 1)) + 1) - (L >= 1 ? floor_log2_u64((uint64_t)L) + 1 : 0);
+            total += cnt * (2 + L - c) + (sum_floor_log2(i - 1) - sum_floor_log2(L)) + kf * (cnt - pow2);
+        }
+        return total;
+    }
+    case BSA_ROUTE_BLOCK_DIAGONAL:
+        return i;
+    case BSA_ROUTE_DENSE_CAUSAL:
+        return i * (i + 1) / 2;
+    case BSA_ROUTE_STATIC_RANDOM:
+        // row 0 holds 1 entry; row r >= 1 holds 1 + kf + min(n_random, r - kf)
+        return 1 + (i - 1) * (1 + kf) + sum_min_cap(i - 1 - kf, n_random);
+    case BSA_ROUTE_SLIDING_WINDOW:
+        return i + sum_min_cap(i - 1, n_local);
     default:
         return -1;
     }

@@ -129,7 +129,9 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
     auto col_load = [&](const Item& it, int t) -> int { return cidx[it.e0 + t]; };
     auto col_use = [&](const Item& it, int raw) -> int64_t {
         const int64_t j = __builtin_amdgcn_readfirstlane(raw);
-        return (j < 0 || j > it.i) ? -1 : j;  // malformed (non-causal) entry: a fully masked chunk
+        // A malformed entry (outside [0, i]) is read as block i: every access stays in bounds, and
+        // results are defined only for valid routes (bsa_check_route).
+        return (j < 0 || j > it.i) ? -1 : j;
     };
     // first global row of chunk `ch` of key block j (an entry outside [0, i] reads block i)
     auto chunk_row = [&](const Item& it, int64_t j, int ch) -> int64_t {
@@ -451,7 +453,9 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
         } else if (nxt.ok) {
             load_q_into(qn, nxt);
         }
-        pref = nxt_chunks;
+        // the next item's first chunk was issued during this item's last chunk; an empty row
+        // (malformed route) issued nothing, so the next item copies its first chunk itself
+        pref = nxt_chunks && L > 0;
         // this wavefront's copies of the next item's first chunk and its next Q have landed;
         // the stores below are left in flight.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -1,9 +1,9 @@
 // route.hip — integer kernels that write a CSR route (row_ptr, col_idx) on the device.
 //
-// Route kinds and their sets are documented with bsa_route_kind in bsa.h.  Two launches:
-//   1. route_rowptr_kernel — one work-group: closed-form row counts, block-wide exclusive scan.
-//   2. route_fill_kernel   — one wavefront per query block: writes that row's key blocks in
-//                            strictly ascending order (self block last).
+// Route kinds and their sets are documented with bsa_route_kind in bsa.h.  One launch,
+// route_build_kernel: one wavefront per query block writes that row's pointer (the closed-form
+// start of every row, route_row_start, so no scan is needed) and its key blocks in strictly
+// ascending order (self block last).
 // Planning is kept apart from the attention kernel, as the BF1 summary times topology
 // separately from the sparse kernel ("BF1 ...", section 4 "Kernel and prefill evaluation").
 
@@ -13,33 +13,6 @@ namespace bsa {
 namespace {
 
 constexpr int kScanThreads = 1024;
-
-__global__ __launch_bounds__(kScanThreads) void route_rowptr_kernel(bsa_route_spec spec, int64_t nqb,
-                                                                    int32_t* __restrict__ row_ptr) {
-    __shared__ int64_t part[kScanThreads];
-    const int t = threadIdx.x;
-    const int64_t per = (nqb + kScanThreads - 1) / kScanThreads;
-    const int64_t r0 = t * per;
-    const int64_t r1 = (r0 + per < nqb) ? r0 + per : nqb;
-    int64_t local = 0;
-    for (int64_t i = r0; i < r1; ++i)
-        local += route_row_count(spec.kind, i, spec.n_local, spec.keep_first, spec.n_random);
-    part[t] = local;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the per-thread sums
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        const int64_t add = (t >= off) ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += add;
-        __syncthreads();
-    }
-    int64_t run = part[t] - local;  // exclusive prefix of this thread's rows
-    if (t == 0) row_ptr[0] = 0;
-    for (int64_t i = r0; i < r1; ++i) {
-        run += route_row_count(spec.kind, i, spec.n_local, spec.keep_first, spec.n_random);
-        row_ptr[i + 1] = (int32_t)run;
-    }
-}
 
 // First SplitMix64 output from state x (golden-ratio increment, then the variant-13 finaliser).
 __device__ inline uint64_t splitmix64(uint64_t x) {
@@ -64,13 +37,18 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t x, int m) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-__global__ __launch_bounds__(64) void route_fill_kernel(bsa_route_spec spec, int64_t nqb,
-                                                        const int32_t* __restrict__ row_ptr,
-                                                        int32_t* __restrict__ col_idx) {
+// One wavefront per query block i (and one for row_ptr[0] when nqb == 0).
+__global__ __launch_bounds__(64) void route_build_kernel(bsa_route_spec spec, int64_t nqb,
+                                                         int32_t* __restrict__ row_ptr,
+                                                         int32_t* __restrict__ col_idx) {
     const int64_t i = blockIdx.x;
     const int lane = threadIdx.x;
+    if (i == 0 && lane == 0) row_ptr[0] = 0;
     if (i >= nqb) return;
-    int32_t* out = col_idx + row_ptr[i];
+    const int64_t start = route_row_start(spec.kind, i, spec.n_local, spec.keep_first, spec.n_random);
+    if (lane == 0)
+        row_ptr[i + 1] = (int32_t)(start + route_row_count(spec.kind, i, spec.n_local, spec.keep_first, spec.n_random));
+    int32_t* out = col_idx + start;
 
     if (spec.kind == BSA_ROUTE_BLOCK_DIAGONAL) {
         if (lane == 0) out[0] = (int32_t)i;
@@ -190,8 +168,11 @@ __global__ __launch_bounds__(64) void route_t_count_kernel(const int32_t* __rest
     if (lane == 0) t_row_ptr[j + 1] = cnt;
 }
 
-// one work-group: in-place inclusive scan of t_row_ptr[1..nqb]; t_row_ptr[0] = 0
-__global__ __launch_bounds__(kScanThreads) void route_t_scan_kernel(int64_t nqb, int32_t* __restrict__ t_row_ptr) {
+// one work-group: in-place inclusive scan of t_row_ptr[1..nqb]; t_row_ptr[0] = 0.  Every prefix is
+// clamped to nnz: rows that overlap (a row_ptr that decreases) can count more memberships than the
+// route has entries, and the fill must never write past the caller's nnz-entry t_col_idx.
+__global__ __launch_bounds__(kScanThreads) void route_t_scan_kernel(int64_t nqb, int64_t nnz,
+                                                                    int32_t* __restrict__ t_row_ptr) {
     __shared__ int64_t part[kScanThreads];
     const int t = threadIdx.x;
     const int64_t per = (nqb + kScanThreads - 1) / kScanThreads;
@@ -210,7 +191,7 @@ __global__ __launch_bounds__(kScanThreads) void route_t_scan_kernel(int64_t nqb,
     int64_t run = part[t] - local;
     for (int64_t x = r0; x < r1; ++x) {
         run += t_row_ptr[x + 1];
-        t_row_ptr[x + 1] = (int32_t)run;
+        t_row_ptr[x + 1] = (int32_t)(run < nnz ? run : nnz);
     }
     if (t == 0) t_row_ptr[0] = 0;
 }
@@ -229,7 +210,7 @@ __global__ __launch_bounds__(64) void route_t_fill_kernel(const int32_t* __restr
         const bool sel = i < nqb && row_holds(row_ptr, col_idx, nnz, i, (int32_t)j);
         const uint64_t mask = __ballot(sel);
         const int pos = __popcll(mask & ((1ull << lane) - 1ull));
-        if (sel && w + pos < end) t_col_idx[w + pos] = (int32_t)i;
+        if (sel && w + pos < end && w + pos < nnz) t_col_idx[w + pos] = (int32_t)i;
         w += __popcll(mask);
     }
 }
@@ -239,14 +220,14 @@ __global__ __launch_bounds__(64) void route_t_fill_kernel(const int32_t* __restr
 hipError_t launch_route_transpose(const int32_t* row_ptr, const int32_t* col_idx, int64_t nqb, int64_t nnz,
                                   int32_t* t_row_ptr, int32_t* t_col_idx, hipStream_t stream) {
     if (nqb == 0) {
-        hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, t_row_ptr);
+        hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, nnz, t_row_ptr);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(route_t_count_kernel, dim3((unsigned)nqb), dim3(64), 0, stream, row_ptr, col_idx, nqb, nnz,
                        t_row_ptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, t_row_ptr);
+    hipLaunchKernelGGL(route_t_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, nqb, nnz, t_row_ptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(route_t_fill_kernel, dim3((unsigned)nqb), dim3(64), 0, stream, row_ptr, col_idx, nqb, nnz,
@@ -256,11 +237,8 @@ hipError_t launch_route_transpose(const int32_t* row_ptr, const int32_t* col_idx
 
 hipError_t launch_route_build(const bsa_route_spec& spec, int64_t nqb, int32_t* row_ptr,
                               int32_t* col_idx, hipStream_t stream) {
-    hipLaunchKernelGGL(route_rowptr_kernel, dim3(1), dim3(kScanThreads), 0, stream, spec, nqb, row_ptr);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || nqb == 0) return e;
-    hipLaunchKernelGGL(route_fill_kernel, dim3((unsigned)nqb), dim3(64), 0, stream, spec, nqb, row_ptr,
-                       col_idx);
+    hipLaunchKernelGGL(route_build_kernel, dim3((unsigned)(nqb > 0 ? nqb : 1)), dim3(64), 0, stream, spec, nqb,
+                       row_ptr, col_idx);
     return hipGetLastError();
 }
 

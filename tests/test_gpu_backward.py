@@ -37,13 +37,36 @@ def transpose_sets(rp, ci):
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("n,B", [(1, 64), (1000, 64), (4097, 128), (32768, 128)])
 def test_route_transpose_bit_exact(kind, n, B):
-    if kind == R.DENSE_CAUSAL and n > 5000:
-        pytest.skip("dense route at 256 blocks is covered at the smaller sizes")
     (rp, ci), (orp, oci) = routes(kind, n, B)
     trp, tci = bsa.build_route_transpose(rp, ci)
     torch.cuda.synchronize()
     want_rp, want_ci = R.to_csr(transpose_sets(orp, oci))
     assert np.array_equal(trp.cpu().numpy(), want_rp) and np.array_equal(tci.cpu().numpy(), want_ci)
+
+
+CANARY = -123456789
+
+
+@pytest.mark.parametrize("row_ptr,col_idx", [
+    ([0, 2, 0, 2], [0, 2]),            # overlapping rows: 4 memberships counted for 2 entries
+    ([0, 3, 1, 3], [0, 1, 2]),         # a row that starts inside the previous one
+    ([0, 1, 9, 9], [0, 1, 1, 2]),      # a row pointer past nnz (clamped on read)
+])
+def test_route_transpose_malformed_stays_in_bounds(row_ptr, col_idx):
+    """The transpose of a malformed route is meaningless, but every write stays inside the caller's
+    buffers: canaries right after t_col_idx[nnz - 1] survive and every t_row_ptr value is <= nnz."""
+    nqb, nnz = len(row_ptr) - 1, len(col_idx)
+    print(f"malformed transpose: row_ptr={row_ptr} col_idx={col_idx}", flush=True)
+    rp = torch.tensor(row_ptr, dtype=torch.int32, device="cuda")
+    ci = torch.tensor(col_idx, dtype=torch.int32, device="cuda")
+    trp_buf = torch.full((nqb + 1 + 64,), CANARY, dtype=torch.int32, device="cuda")
+    tci_buf = torch.full((nnz + 64,), CANARY, dtype=torch.int32, device="cuda")
+    bsa.bsa_build_route_transpose(rp, ci, trp_buf[:nqb + 1], tci_buf[:nnz])
+    torch.cuda.synchronize()
+    trp = trp_buf.cpu().numpy()
+    tci = tci_buf.cpu().numpy()
+    assert (trp[nqb + 1:] == CANARY).all() and (tci[nnz:] == CANARY).all()
+    assert trp[0] == 0 and (np.diff(trp[:nqb + 1]) >= 0).all() and trp[nqb] <= nnz
 
 
 def grad_errors(got, ref):
