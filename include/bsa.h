@@ -250,6 +250,30 @@ bsa_status bsa_decode_routed(const void* q, const void* k_cache, const void* v_c
                              hipStream_t stream);
 
 /*
+ * bsa_decode_routed_noalloc — bsa_decode_routed without a workspace argument, for callers that
+ * cannot allocate device memory: code under stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The fp32 partials go to the library's static scratch array instead, a
+ * device-resident array of BSA_STATIC_SCRATCH_BYTES that every device the library runs on holds
+ * from its first call until the process ends.  The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).  Same arguments (minus workspace and
+ * workspace_bytes), kernels, arithmetic and output as bsa_decode_routed: bit for bit equal to it.
+ * Limit: the partials need batch * heads_q * splits * (d + 2) * 4 bytes, where the split count
+ * (at most 64) is the one bsa_decode_routed chooses; beyond BSA_STATIC_SCRATCH_BYTES the call
+ * returns BSA_ERR_CAPACITY before any device work (e.g. at d = 128 and 64 splits, up to 252
+ * (batch, query head) pairs).  Every slot the merge reads is written by the same call, so the
+ * array's contents on entry do not matter.  All calls on one device share its array: calls that
+ * overlap in time on one device (on different streams, or from different threads without
+ * ordering) race and give undefined results; calls ordered on one stream are safe.
+ * Errors: as bsa_decode_routed, plus BSA_ERR_CAPACITY (array too small) and BSA_ERR_DEVICE
+ * (symbol lookup or launch failure).
+ */
+#define BSA_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+bsa_status bsa_decode_routed_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                     const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                     int64_t n_max, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                                     const bsa_route_spec* spec, hipStream_t stream);
+
+/*
  * bsa_bsbr_forward — BSBR attention ("bsbr", Solution: the combined formula), chunks of
  * `chunk` tokens, nch = ceil(n / chunk):
  *

@@ -280,12 +280,13 @@ size_t bsa_decode_workspace_bytes(int32_t batch, int32_t heads_q, int32_t d) {
 
 namespace {
 
-// Shared by bsa_decode (CSR route: row_ptr/col_idx/nnz) and bsa_decode_routed (spec).
+// Shared by bsa_decode (CSR route: row_ptr/col_idx/nnz), bsa_decode_routed (spec) and
+// bsa_decode_routed_noalloc (spec, the library's static scratch array: static_ws).
 bsa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                        const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n_max,
                        int32_t d, int32_t block, bsa_dtype dtype, float scale, const int32_t* row_ptr,
                        const int32_t* col_idx, int64_t nnz, const bsa_route_spec* spec, float* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       size_t workspace_bytes, hipStream_t stream, bool static_ws = false) {
     if (batch < 0 || heads_q < 1 || heads_kv < 1 || n_max < 1 || block < 1 || d < 1)
         return fail(BSA_ERR_INVALID_ARGUMENT,
                     "sizes must satisfy batch >= 0, heads >= 1, n_max >= 1, d >= 1, block >= 1 "
@@ -307,16 +308,19 @@ bsa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, 
         if (spec->n_local < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "n_local must be >= 0");
     }
     if (batch == 0) return ok();
-    if (!q || !k_cache || !v_cache || !o || !seq_lens || !workspace || (!spec && (!row_ptr || !col_idx)))
+    if (!q || !k_cache || !v_cache || !o || !seq_lens || (!static_ws && !workspace) || (!spec && (!row_ptr || !col_idx)))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o, seq_lens, route and workspace must be non-NULL");
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(workspace))
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        (!static_ws && !aligned16(workspace)))
         return fail(BSA_ERR_INVALID_ARGUMENT, "q, k_cache, v_cache, o and workspace must be 16-byte aligned");
     if (lse && ((uintptr_t)lse & 3u)) return fail(BSA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
     if (((uintptr_t)seq_lens & 3u) != 0) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
     if (!spec && (nnz < nqb || nnz > INT32_MAX))
         return fail(BSA_ERR_INVALID_ARGUMENT, "nnz=%lld must be in [nqb=%lld, 2^31)", (long long)nnz, (long long)nqb);
-    const size_t need = bsa_decode_workspace_bytes(batch, heads_q, d);
-    if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
+    if (!static_ws) {
+        const size_t need = bsa_decode_workspace_bytes(batch, heads_q, d);
+        if (workspace_bytes < need) return fail(BSA_ERR_CAPACITY, "workspace_bytes %zu < %zu", workspace_bytes, need);
+    }
 
     bsa::DecodeParams p;
     p.q = q; p.k = k_cache; p.v = v_cache; p.o = o; p.lse = lse;
@@ -343,6 +347,20 @@ bsa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, 
     p.splits = (int32_t)S;
     if (base_units * S > INT32_MAX || (int64_t)batch * heads_q > INT32_MAX)
         return fail(BSA_ERR_UNSUPPORTED, "grid too large");
+    if (static_ws) {
+        // the partials of this call: every slot the merge reads is written by the same call, so
+        // nothing in the array needs clearing
+        const size_t need = (size_t)batch * heads_q * S * (d + 2) * sizeof(float);
+        if (need > BSA_STATIC_SCRATCH_BYTES)
+            return fail(BSA_ERR_CAPACITY,
+                        "decode partials need %zu bytes (batch %d x heads_q %d x %lld splits x (d + 2) floats), "
+                        "more than the %zu-byte static scratch array: use bsa_decode_routed with a workspace",
+                        need, batch, heads_q, (long long)S, (size_t)BSA_STATIC_SCRATCH_BYTES);
+        void* ptr = nullptr;
+        const hipError_t e = bsa::static_scratch(&ptr);
+        if (e != hipSuccess) return device_error(e, "static scratch lookup");
+        p.ws = (float*)ptr;
+    }
     const double sc = (scale > 0.f) ? (double)scale : 1.0 / std::sqrt((double)d);
     p.scale_log2 = (float)(sc * 1.4426950408889634073599);
     const hipError_t e = bsa::launch_decode(p, d, dtype == BSA_BF16, stream);
@@ -369,6 +387,15 @@ bsa_status bsa_decode_routed(const void* q, const void* k_cache, const void* v_c
     if (!spec) return fail(BSA_ERR_INVALID_ARGUMENT, "spec must be non-NULL");
     return decode_impl(q, k_cache, v_cache, o, lse, seq_lens, batch, heads_q, heads_kv, n_max, d, block, dtype,
                        scale, nullptr, nullptr, 0, spec, workspace, workspace_bytes, stream);
+}
+
+bsa_status bsa_decode_routed_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                     const int32_t* seq_lens, int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                     int64_t n_max, int32_t d, int32_t block, bsa_dtype dtype, float scale,
+                                     const bsa_route_spec* spec, hipStream_t stream) {
+    if (!spec) return fail(BSA_ERR_INVALID_ARGUMENT, "spec must be non-NULL");
+    return decode_impl(q, k_cache, v_cache, o, lse, seq_lens, batch, heads_q, heads_kv, n_max, d, block, dtype,
+                       scale, nullptr, nullptr, 0, spec, nullptr, 0, stream, true);
 }
 
 size_t bsa_dense_route_workspace_bytes(int64_t n, int32_t block) {

@@ -218,6 +218,10 @@ int64_t bwd_segments_upper_bound(int64_t nqb, int64_t nnz, int heads_q, int head
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, int block, hipStream_t stream);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream);
+
+// Device address of the current device's copy of the library's static scratch array
+// (BSA_STATIC_SCRATCH_BYTES), looked up once per device (static_scratch.hip).
+hipError_t static_scratch(void** ptr);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t stream);
 hipError_t launch_fwd_bf16_basic(const FwdParams& p, int d, int block, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, int block, hipStream_t stream);

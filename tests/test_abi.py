@@ -152,6 +152,21 @@ def test_decode_routed_empty_batch_and_no_route_pointers():
                                   ws=None) == bsa.BSA_OK
 
 
+def test_decode_routed_noalloc_rejects_before_device_work():
+    L = bsa.lib()
+    spec = bsa.route_spec(bsa.BSA_ROUTE_BF1)
+    # 512 x 64 (batch, query head) pairs of single-split partials at d = 128 need 17 MB, more
+    # than the static scratch array holds: refused before any device call (this runs without a GPU)
+    st = L.bsa_decode_routed_noalloc(16, 16, 16, 16, None, 16, 512, 64, 64, 65536, 128, 128, 0, 0.0,
+                                     ctypes.byref(spec), None)
+    assert st == bsa.BSA_ERR_CAPACITY and "static scratch" in bsa.bsa_last_error()
+    assert L.bsa_decode_routed_noalloc(16, 16, 16, 16, None, 16, 2, 4, 2, 1000, 128, 128, 0, 0.0, None,
+                                       None) == bsa.BSA_ERR_INVALID_ARGUMENT
+    st = L.bsa_decode_routed_noalloc(None, None, None, None, None, None, 0, 4, 2, 1000, 128, 128, 0, 0.0,
+                                     ctypes.byref(spec), None)
+    assert st == bsa.BSA_OK  # empty batch: nothing to do
+
+
 def test_dense_ref_rejects_small_workspace():
     L = bsa.lib()
     need = bsa.bsa_dense_route_workspace_bytes(4096, 64)
