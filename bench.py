@@ -357,14 +357,17 @@ def bsbr_bench(steps: int) -> dict:
     return out
 
 
-def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
-    """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload."""
+def cpu_baseline(w, q, k, v, target_s: float = 15.0):
+    """Time the fp64 oracle on the host over a bounded sample of query blocks of the workload, on
+    the route oracle/routes.py builds from the workload's parameters (nothing from the GPU)."""
     from oracle import attn as A
+    from oracle import routes as OR
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
     except Exception:
         blas_threads = os.cpu_count() or 1
+    rp, ci = OR.route_csr(w.route_kind, w.n, w.block, **w.route_params())
     nqb = w.nqb
     order = np.linspace(0, nqb - 1, num=min(nqb, 64)).round().astype(int)
     done_rows, sel_pairs, t_used, blocks = 0, 0, 0.0, 0
@@ -384,8 +387,49 @@ def cpu_baseline(w, q, k, v, rp, ci, target_s: float = 15.0):
             break
     flops = 4.0 * w.d * w.batch * w.heads_q * sel_pairs
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{blocks} of {nqb} query blocks ({done_rows} query rows x {w.batch * w.heads_q} heads, "
-                      f"spread evenly over the sequence), fp64 masked-dense numpy, {t_used:.1f} s"}
+            "sample": f"{w.name}: {blocks} of {nqb} query blocks ({done_rows} query rows x {w.batch * w.heads_q} "
+                      f"heads, spread evenly over the sequence), fp64 masked-dense numpy on the oracle's own "
+                      f"route, {t_used:.1f} s", "seconds": round(t_used, 2)}
+
+
+def crossover(steps: int) -> dict:
+    """BF1 against the dense causal route on the same inputs at the Qwen3 layer geometry (batch 1,
+    16 query / 8 key-value heads, d 128) for n = 2K .. 32K at block widths 64 and 128: the forward
+    time of each, the speedup, and the ratio of selected causal pairs (dense / BF1).  "BF1 ...",
+    section 5 (per-layer prefill scaling) reports the crossover between 2K and 4K tokens and
+    2.84x / 5.50x / 10.91x at 8K / 16K / 32K on its own hardware (context, not a target)."""
+    import torch
+    import long_context_block_amd as bsa
+    import synth
+    base = synth.WORKLOADS["qwen3_32k"]
+    rows = []
+    for n in (2048, 4096, 8192, 16384, 32768):
+        w0 = base.resized(name=f"qwen3_{n // 1024}k", n=n)
+        q, k, v = (x.cuda() for x in synth.make_qkv(w0))
+        o = torch.empty_like(q)
+        for B in (64, 128):
+            w = w0.resized(block=B)
+            rp, ci = bsa.build_route(bsa.route_spec(bsa.BSA_ROUTE_BF1, w.n_local, w.keep_first), n, B)
+            drp, dci = bsa.build_route(bsa.route_spec(bsa.BSA_ROUTE_DENSE_CAUSAL), n, B)
+            torch.cuda.synchronize()
+            S = selected_pairs(rp.cpu().numpy(), ci.cpu().numpy(), n, B)
+            S_dense = n * (n + 1) // 2
+            f_bf1 = lambda: bsa.bsa_forward(q, k, v, o, rp, ci, B)  # noqa: E731
+            f_dense = lambda: bsa.bsa_forward(q, k, v, o, drp, dci, B)  # noqa: E731
+            reps = max(5, steps // (4 if n >= 16384 else 1))
+            ms_bf1 = min(time_loop(f_bf1, reps, 3), time_loop(f_bf1, reps, 1))
+            ms_dense = min(time_loop(f_dense, max(3, reps // 4), 2), time_loop(f_dense, max(3, reps // 4), 1))
+            fl = 4.0 * w.d * w.batch * w.heads_q
+            rows.append({"n": n, "block": B, "bf1_ms": round(ms_bf1, 5), "dense_ms": round(ms_dense, 5),
+                         "speedup": round(ms_dense / ms_bf1, 3), "pair_ratio": round(S_dense / S, 3),
+                         "bf1_selected_tflops": round(fl * S / (ms_bf1 * 1e-3) / 1e12, 1),
+                         "dense_tflops": round(fl * S_dense / (ms_dense * 1e-3) / 1e12, 1),
+                         "nnz_bf1": int(ci.numel())})
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    return {"geometry": "batch 1, 16/8 heads, d 128, BF1 n_local 2 with block 0, bf16", "rows": rows,
+            "pages_speedup_context": {"8192": 2.84, "16384": 5.50, "32768": 10.91},
+            "pages_crossover_context": "between 2K and 4K tokens"}
 
 
 def main():
@@ -530,8 +574,16 @@ def main():
         out["backward"] = backward_bench(w, qd, kd, vd, args.steps)
         out["other_workloads"] = other_workloads([x for x in synth.WORKLOADS if x != w.name], args.steps)
         out["bsbr"] = bsbr_bench(args.steps)
+    if not args.no_others:
+        out["crossover"] = crossover(args.steps)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, rp_h, ci_h, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        if not args.no_others:
+            out["cpu_baseline_other_workloads"] = {
+                x: {key: val for key, val in cpu_baseline(synth.WORKLOADS[x], *synth.make_qkv(synth.WORKLOADS[x]),
+                                                        target_s=max(1.0, args.cpu_seconds / 5)).items()
+                    if key in ("value", "unit", "cores", "sample", "seconds")}
+                for x in synth.WORKLOADS if x != w.name}
     print(json.dumps(out), flush=True)
 
 

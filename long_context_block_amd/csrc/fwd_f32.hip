@@ -76,6 +76,7 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
             __syncthreads();
             float sc[kKeyChunk];
             float cmax = -INFINITY;
+            bool has_nan = false;  // fmaxf drops NaN: a NaN score is tracked apart and poisons the row
 #pragma unroll
             for (int r = 0; r < kKeyChunk; ++r) {
                 float part = 0.f;
@@ -92,9 +93,10 @@ __global__ __launch_bounds__(kF32Threads) void fwd_f32_kernel(FwdParams p) {
                 if (diag && (kc + r > rloc)) s2 = -INFINITY;  // causal mask inside the diagonal block
                 sc[r] = s2;
                 cmax = fmaxf(cmax, s2);
+                has_nan |= (s2 != s2);
             }
-            if (cmax == -INFINITY) continue;  // whole chunk masked for this row
-            const float m_new = fmaxf(m_run, cmax);
+            if (cmax == -INFINITY && !has_nan) continue;  // whole chunk masked for this row
+            const float m_new = has_nan ? NAN : fmaxf(m_run, cmax);  // NaN: running sum and output go NaN
             const float alpha = exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll

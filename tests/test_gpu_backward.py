@@ -143,6 +143,18 @@ def test_backward_deterministic_and_no_future_gradient():
     dq, dk, dv = bsa.backward(q, k, v, o, d_o2, lse, rp, ci, w.block)
     torch.cuda.synchronize()
     assert (dq[:, :, :800] == 0).all()
+    # keys and values read by none of those rows get exactly zero gradient; the ones they read get
+    # some (rows 800 .. 899 lie in query blocks 6 and 7, which read their routes' key blocks, and
+    # within block 6 only the keys up to row 899)
+    sets = R.csr_to_sets(rp.cpu().numpy(), ci.cpu().numpy())
+    read = np.zeros(w.n, dtype=bool)
+    for i in (800 // w.block, (w.n - 1) // w.block):
+        for j in sets[i]:
+            read[j * w.block:(j + 1) * w.block] = True
+    read_t = torch.from_numpy(read).cuda()
+    for g in (dk, dv):
+        assert (g[:, :, ~read_t] == 0).all()
+        assert (g[:, :, read_t].abs().amax(dim=-1) > 0).all()
 
 
 def test_backward_errors():
@@ -192,3 +204,31 @@ def test_backward_transposed_rows_in_any_order(wname, n):
         print(f"  reversed rows {name}: rel-L2 {rl2:.3e} max-abs/max {mx:.3e}", flush=True)
         assert rl2 <= RELL2 and mx <= MAXREL, (name, rl2, mx)
     assert torch.equal(grads[0][0], grads[1][0])  # dQ walks the forward route: unaffected
+
+
+def test_canary_padded_gradients_and_workspace():
+    """No store outside dq, dk, dv or the workspace, and every gradient element written, at partial
+    final blocks for both kernels' block widths."""
+    from canary import padded, padded_workspace
+    for w in (synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-d128-b128-n1000", n=1000, heads_q=4, heads_kv=2),
+              synth.WORKLOADS["bf1_4k"].resized(name="mha-d128-b64-n129", n=129, heads_q=2, heads_kv=2),
+              synth.WORKLOADS["bf1_4k"].resized(name="gqa4-d64-b64-n70", n=70, d=64, heads_q=4, heads_kv=1)):
+        print(f"canary backward {w.name}", flush=True)
+        q, k, v = (x.cuda() for x in synth.make_qkv(w))
+        d_o = torch.randn(q.shape, device="cuda").to(q.dtype)
+        (rp, ci), _ = workload_routes(w)
+        o, lse = bsa.forward(q, k, v, rp, ci, w.block, with_lse=True)
+        trp, tci = bsa.build_route_transpose(rp, ci)
+        b, hq, n, d = q.shape
+        dq, dk, dv = padded(q.shape, q.dtype), padded(k.shape, k.dtype), padded(v.shape, v.dtype)
+        ws = padded_workspace(bsa.bsa_backward_workspace_bytes(b, hq, k.shape[1], n, d, w.block, ci.numel()))
+        bsa.bsa_backward(q, k, v, o, d_o, lse, dq.t, dk.t, dv.t, rp, ci, trp, tci, w.block, ws.t)
+        torch.cuda.synchronize()
+        for x in (dq, dk, dv, ws):
+            assert x.guards_intact()
+        for x in (dq, dk, dv):
+            assert not x.untouched().any()
+        ref = bsa.backward(q, k, v, o, d_o, lse, rp, ci, w.block)
+        torch.cuda.synchronize()
+        for x, r in zip((dq, dk, dv), ref):
+            assert torch.equal(x.t, r)

@@ -125,3 +125,22 @@ def test_bsbr_errors():
     assert e.value.status == bsa.BSA_ERR_CAPACITY
     with pytest.raises(ValueError):  # meta tensors must have one row per chunk
         bsa.bsa_bsbr_forward(qb, qb, qb, rb[:, :, :1], rb, qb.clone(), 128, ws)
+
+
+@pytest.mark.parametrize("w", [CASES[1], CASES[2], CASES[4]], ids=[CASES[i].name for i in (1, 2, 4)])
+def test_bsbr_canary_padded(w):
+    """No store outside o or the workspace, and every output element written, at partial final
+    chunks."""
+    from canary import padded, padded_workspace
+    print(f"bsbr canary {w.name}", flush=True)
+    q, k, v = (x.cuda() for x in synth.make_qkv(w))
+    r, h = (x.cuda() for x in synth.make_meta(w))
+    o = padded(q.shape, q.dtype)
+    ws = padded_workspace(bsa.bsa_bsbr_workspace_bytes(w.batch, w.heads_q, w.heads_kv, w.n, w.d, w.block))
+    bsa.bsa_bsbr_forward(q, k, v, r, h, o.t, w.block, ws.t)
+    torch.cuda.synchronize()
+    assert o.guards_intact() and ws.guards_intact()
+    assert not o.untouched().any()
+    ref = bsa.bsbr_forward(q, k, v, r, h, w.block)
+    torch.cuda.synchronize()
+    assert torch.equal(o.t, ref)

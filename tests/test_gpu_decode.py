@@ -212,3 +212,33 @@ def test_decode_routed_errors():
     with pytest.raises(bsa.BsaError) as e:
         bsa.bsa_decode_routed(q, k, k, torch.empty_like(q), sl, bsa.route_spec(R.BF1), 64, ws[:8])
     assert e.value.status == bsa.BSA_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[3]], ids=[CASES[i][0] for i in (0, 1, 3)])
+def test_decode_canary_padded(case):
+    """No store outside o, lse or the workspace, and every output element written, with the plan
+    from a CSR route and from the in-kernel rows."""
+    from canary import padded, padded_workspace
+    name, batch, hq, hkv, n_max, d, B, dt = case
+    q, k, v = (x.cuda() for x in make(batch, hq, hkv, n_max, d, dt, seed=33))
+    lens = torch.tensor([n_max, 1, B + 1][:batch], dtype=torch.int32, device="cuda")
+    (rp, ci), _ = routes(R.BF1, n_max, B, 2, 1, 14, 17)
+    for routed in (False, True):
+        print(f"decode canary {name} routed={routed}", flush=True)
+        o, lse = padded(q.shape, q.dtype), padded((batch, hq), torch.float32)
+        ws = padded_workspace(bsa.bsa_decode_workspace_bytes(batch, hq, d), torch.float32)
+        if routed:
+            bsa.bsa_decode_routed(q, k, v, o.t, lens, bsa.route_spec(R.BF1), B, ws.t, lse=lse.t)
+        else:
+            bsa.bsa_decode(q, k, v, o.t, lens, rp, ci, B, ws.t, lse=lse.t)
+        torch.cuda.synchronize()
+        for x in (o, lse, ws):
+            assert x.guards_intact()
+        assert not o.untouched().any() and not lse.untouched().any()
+        # the same entry point on plain buffers (the two entry points may split the keys differently)
+        if routed:
+            ref, ref_lse = bsa.decode_routed(q, k, v, lens, bsa.route_spec(R.BF1), B, with_lse=True)
+        else:
+            ref, ref_lse = bsa.decode(q, k, v, lens, rp, ci, B, with_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o.t, ref) and torch.equal(lse.t, ref_lse)

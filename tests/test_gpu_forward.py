@@ -259,3 +259,135 @@ def test_validate_route_env(monkeypatch):
     with pytest.raises(bsa.BsaError) as e:
         bsa.forward(q, k, v, rp, bad, w.block)
     assert e.value.status == bsa.BSA_ERR_BAD_ROUTE
+
+
+def test_dense_causal_ref_against_the_oracle_full_size_sampled():
+    # bsa_dense_causal_ref (route built inside the call) against the oracle's dense causal
+    # attention on sampled rows of the 32K GQA workload
+    w = synth.WORKLOADS["qwen3_32k"]
+    q, k, v = synth.make_qkv(w)
+    ws = torch.empty(bsa.bsa_dense_route_workspace_bytes(w.n, w.block) // 4, dtype=torch.int32, device="cuda")
+    o = torch.empty(q.shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    bsa.bsa_dense_causal_ref(q.cuda(), k.cuda(), v.cuda(), o, ws, w.block, lse=lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.n, w.block, np.random.default_rng(11), extra=8)
+    orp, oci = R.route_csr(R.DENSE_CAUSAL, w.n, w.block)
+    ref, ref_lse = A.attention(q, k, v, w.block, orp, oci, rows=rows, return_lse=True)
+    mx, rl2 = errors(o.float().cpu().numpy()[:, :, rows], ref)
+    lse_err = float(np.abs(lse.cpu().numpy()[:, :, rows] - ref_lse).max())
+    print(f"dense_causal_ref 32K: max-abs {mx:.3e} rel-L2 {rl2:.3e} lse {lse_err:.3e}", flush=True)
+    assert mx <= BF16_MAXABS and rl2 <= BF16_RELL2 and lse_err <= 2.5e-3
+
+
+# ---- canary-padded outputs: no store outside O and LSE, and every element of both written ------
+
+CANARY_CASES = [
+    # (name, batch, heads_q, heads_kv, n, d, block, dtype)
+    ("gqa2-d128-b128-n129", 1, 2, 1, 129, 128, 128, "bf16"),
+    ("gqa2-d64-b128-n1000", 2, 4, 2, 1000, 64, 128, "bf16"),
+    ("mha-d64-b64-n1", 1, 2, 2, 1, 64, 64, "bf16"),
+    ("mha-d128-b64-n777", 1, 2, 2, 777, 128, 64, "bf16"),
+    ("gqa4-d64-b64-n65", 1, 4, 1, 65, 64, 64, "bf16"),
+    ("mha-d64-b128-n300", 2, 2, 2, 300, 64, 128, "bf16"),
+    ("mha-d128-b128-n300-fp32", 1, 2, 2, 300, 128, 128, "fp32"),
+    ("gqa2-d64-b64-n100-fp32", 1, 2, 1, 100, 64, 64, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", CANARY_CASES, ids=[c[0] for c in CANARY_CASES])
+@pytest.mark.parametrize("dense_ref", [False, True])
+def test_canary_padded_outputs(case, dense_ref):
+    from canary import padded
+    name, batch, hq, hkv, n, d, B, dtype = case
+    w = synth.WORKLOADS["qwen3_32k"].resized(name=name, batch=batch, heads_q=hq, heads_kv=hkv, n=n, d=d,
+                                             block=B, dtype=dtype)
+    print(f"canary {name} dense_ref={dense_ref}", flush=True)
+    q, k, v = synth.make_qkv(w)
+    kind = R.DENSE_CAUSAL if dense_ref else w.route_kind
+    (rp, ci), (orp, oci) = workload_routes(w, kind)
+    o = padded(q.shape, q.dtype)
+    lse = padded(q.shape[:3], torch.float32)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    if dense_ref:
+        ws = torch.empty(bsa.bsa_dense_route_workspace_bytes(n, B) // 4, dtype=torch.int32, device="cuda")
+        bsa.bsa_dense_causal_ref(qd, kd, vd, o.t, ws, B, lse=lse.t)
+    else:
+        bsa.bsa_forward(qd, kd, vd, o.t, rp, ci, B, lse=lse.t)
+    torch.cuda.synchronize()
+    assert o.guards_intact() and lse.guards_intact()
+    assert not o.untouched().any() and not lse.untouched().any()
+    ref, ref_lse = A.attention(q, k, v, B, orp, oci, return_lse=True)
+    mx, rl2 = errors(o.t.float().cpu().numpy(), ref)
+    ma, rt = tol(w.torch_dtype)
+    assert mx <= ma and rl2 <= rt
+    assert float(np.abs(lse.t.cpu().numpy() - ref_lse).max()) <= (1e-5 if dtype == "fp32" else 2.5e-3)
+
+
+# ---- NaN inputs reach only the rows that read them -------------------------------------------
+# A NaN in q row r makes output row r NaN.  A NaN in element c of key j makes NaN every row whose
+# selected keys include j (its score is NaN); a NaN in element c of value j makes element c NaN in
+# those rows.  Rows of a query block whose route lists j's key block but that do not select j
+# (within the diagonal block, the rows before j) may take the NaN as well: their zero weight
+# multiplies value j in the same matrix product.  Every other output element, and the LSE of
+# every row in the value case, is bit-identical to the run without the NaN.
+
+NAN_CASES = [
+    ("gqa2-d128-b128", 1, 4, 2, 700, 128, 128, "bf16"),
+    ("mha-d128-b64", 1, 2, 2, 650, 128, 64, "bf16"),
+    ("gqa2-d64-b128-fp32", 1, 2, 1, 400, 64, 128, "fp32"),
+]
+
+
+@pytest.mark.parametrize("case", NAN_CASES, ids=[c[0] for c in NAN_CASES])
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_nan_reaches_only_the_rows_that_read_it(case, which):
+    name, batch, hq, hkv, n, d, B, dtype = case
+    w = synth.WORKLOADS["qwen3_32k"].resized(name=name, batch=batch, heads_q=hq, heads_kv=hkv, n=n, d=d,
+                                             block=B, dtype=dtype)
+    print(f"nan {name} in {which}", flush=True)
+    q, k, v = synth.make_qkv(w)
+    (rp, ci), (orp, oci) = workload_routes(w)
+    sets = R.csr_to_sets(orp, oci)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o0, lse0 = bsa.forward(qd, kd, vd, rp, ci, B, with_lse=True)
+    G = hq // hkv
+    head, row, col = {"q": (1, n // 2, 5), "k": (hkv - 1, n // 3, 7), "v": (hkv - 1, (2 * n) // 3, 7)}[which]
+    t = {"q": qd, "k": kd, "v": vd}[which].clone()
+    t[0, head, row, col] = float("nan")
+    args = {"q": (t, kd, vd), "k": (qd, t, vd), "v": (qd, kd, t)}[which]
+    o1, lse1 = bsa.forward(*args, rp, ci, B, with_lse=True)
+    torch.cuda.synchronize()
+    a0, a1 = o0.float().cpu().numpy(), o1.float().cpu().numpy()
+    l0, l1 = lse0.cpu().numpy(), lse1.cpu().numpy()
+    must = np.zeros((batch, hq, n), dtype=bool)  # rows that select the NaN element
+    may = np.zeros((batch, hq, n), dtype=bool)   # ... or share a matrix product with it
+    if which == "q":
+        must[0, head, row] = may[0, head, row] = True
+    else:
+        jb = row // B
+        for h in range(head * G, head * G + G):
+            for r in range(n):
+                if jb in sets[r // B]:
+                    may[0, h, r] = True
+                    must[0, h, r] = r >= row
+
+    def same(x, y):  # bit-identical
+        return np.array_equal(np.ascontiguousarray(x, np.float32).view(np.uint32),
+                              np.ascontiguousarray(y, np.float32).view(np.uint32))
+    if which == "v":
+        # element `col` of the rows that select value j is NaN; the other elements and the LSE are untouched
+        assert np.isnan(a1[must][:, col]).all()
+        other = np.ones(d, dtype=bool)
+        other[col] = False
+        assert same(a0[..., other], a1[..., other])
+        assert same(a0[~may][:, col], a1[~may][:, col])
+        mid0, mid1 = a0[may & ~must][:, col], a1[may & ~must][:, col]
+        assert (np.isnan(mid1) | (mid1.view(np.uint32) == mid0.view(np.uint32))).all()
+        assert same(l0, l1)
+    else:
+        assert np.isnan(a1[must]).all() and np.isnan(l1[must]).all()
+        assert same(a0[~may], a1[~may]) and same(l0[~may], l1[~may])
+        for r_ok in zip(*np.nonzero(may & ~must)):  # the rows before j in its diagonal block
+            x0, x1 = a0[r_ok], a1[r_ok]
+            assert np.isnan(x1).all() or same(x0, x1)
