@@ -2,7 +2,7 @@
 """Benchmark: causal block-sparse attention forward (prefill) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_32k] [--no-cpu-baseline]
-                    [--no-others]
+                    [--no-others] [--only backward|bsbr|decode]
 
 Workload (default): the Qwen3-0.6B-shaped layer at 32K tokens — batch 1, 16 query / 8 key-value
 heads, d = 128, block 128, bf16, BF1 route — the geometry the BF1 summary quotes its 32K
@@ -441,6 +441,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads' forward timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["backward", "bsbr", "decode"], default=None,
+                    help="run only this secondary section on the workload's inputs and print it (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="run only a plain device-to-device copy of MB MiB (calibrates rocprofv3 "
                          "FETCH_SIZE/WRITE_SIZE against a known byte count) and exit")
@@ -469,6 +471,12 @@ def main():
     q, k, v = synth.make_qkv(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     od = torch.empty_like(qd)
+    if args.only:
+        sect = {"backward": lambda: backward_bench(w, qd, kd, vd, args.steps),
+                "bsbr": lambda: bsbr_bench(args.steps),
+                "decode": lambda: [decode_bench(w, kd, vd, args.steps, batch) for batch in (1, 16)]}[args.only]
+        print(json.dumps({"workload": w.name, args.only: sect()}), flush=True)
+        return
 
     spec = bsa.route_spec(w.route_kind, w.n_local, w.keep_first, w.n_random, w.route_seed)
     nnz = bsa.bsa_build_route(spec, w.n, w.block)
