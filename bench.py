@@ -12,8 +12,9 @@ HBM when timing starts.
 One step = one pass of the hot path: build the BF1 route (integer kernels) and run the
 block-sparse forward over it.  W untimed warmup steps, then exactly K steps between HIP events
 on the launch stream, bracketed by torch.cuda.synchronize().  Separately timed on the same
-inputs: the forward alone (the dominant kernel, for the roofline), and the same kernel over the
-dense causal route (the speedup denominator), in both orders sparse->dense and dense->sparse.
+inputs: the forward alone (the dominant kernel, for the roofline: K launches right before and right
+after the timed steps, the faster of the two), and the same kernel over the dense causal route
+(the speedup denominator), in both orders sparse->dense and dense->sparse.
 
 Also reported, outside the timed region: the backward pass (BF1 and dense route), selected-page decode of the newest token over the same
 tensors as a key/value cache (batch 1 and 16; persistent plan, plan per token, dense route), the
@@ -302,6 +303,9 @@ def other_workloads(names, steps: int) -> dict:
         S = selected_pairs(rp.cpu().numpy(), ci.cpu().numpy(), w.n, w.block)
         fn = lambda: bsa.bsa_forward(q, k, v, o, rp, ci, w.block)  # noqa: E731
         ms = time_loop(fn, max(10, steps), 5)
+        # the same kernel over the dense causal route on the same inputs (the speedup denominator)
+        drp, dci = bsa.build_route(bsa.route_spec(bsa.BSA_ROUTE_DENSE_CAUSAL), w.n, w.block)
+        ms_dense = time_loop(lambda: bsa.bsa_forward(q, k, v, o, drp, dci, w.block), max(3, steps // 10), 2)
         flops = 4.0 * w.d * w.batch * w.heads_q * S
         nbytes = algorithmic_bytes(w)
         tflops, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
@@ -316,7 +320,8 @@ def other_workloads(names, steps: int) -> dict:
                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}
         out[name] = {"forward_ms": round(ms, 5), "selected_tflops": round(tflops, 3),
                      "algorithmic_bytes": nbytes, "algorithmic_GBs": round(gbs, 1), "nnz": int(ci.numel()),
-                     "roofline": roof}
+                     "selected_pairs_per_head": int(S), "dense_route_ms": round(ms_dense, 5),
+                     "speedup_vs_dense": round(ms_dense / ms, 3), "roofline": roof}
         del q, k, v, o
         torch.cuda.empty_cache()
     return out
@@ -519,9 +524,13 @@ def main():
     ms_fwd_b = time_loop(fwd, args.steps, 3)
     ms_route = time_loop(route_step, args.steps, 3)
     fwd_samples = per_call_samples(fwd, max(20, args.steps))
-    # the timed region: W warmup steps, then K steps (route build + forward)
+    # the timed region: W warmup steps, then K steps (route build + forward), bracketed by the
+    # forward alone, K launches each, so that the kernel's time and the step's are taken under the
+    # same clock conditions
+    ms_fwd_c = time_loop(fwd, args.steps, 3)
     ms_step = time_loop(step, args.steps, args.warmup)
-    ms_fwd = min(ms_fwd_a, ms_fwd_b)
+    ms_fwd_d = time_loop(fwd, args.steps, 3)
+    ms_fwd = min(ms_fwd_c, ms_fwd_d)
     ms_dense = min(ms_dense_a, ms_dense_b)
 
     tflops_step = flops / (ms_step * 1e-3) / 1e12
@@ -567,7 +576,9 @@ def main():
         "dense_route_ms": round(ms_dense, 5),
         "dense_route_tflops": round(tflops_dense, 2),
         "dense_ms_orders": {"sparse_then_dense": round(ms_dense_a, 5), "dense_then_sparse": round(ms_dense_b, 5)},
-        "sparse_ms_orders": {"sparse_then_dense": round(ms_fwd_a, 5), "dense_then_sparse": round(ms_fwd_b, 5)},
+        "sparse_ms_orders": {"sparse_then_dense": round(ms_fwd_a, 5), "dense_then_sparse": round(ms_fwd_b, 5),
+                             "before_step": round(ms_fwd_c, 5), "after_step": round(ms_fwd_d, 5)},
+        "step_minus_forward_ms": round(ms_step - ms_fwd, 5),
         "speedup_vs_dense": round(ms_dense / ms_fwd, 3),
         "ideal_speedup_vs_dense": round(S_dense / S, 3),
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(tflops_fwd, 2),
