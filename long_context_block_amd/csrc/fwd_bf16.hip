@@ -6,17 +6,18 @@
 // Schema": mask before softmax; "BF1 ...", Method: each query block reads itself causally).
 // Key blocks not in the row are never loaded or scored ("Block-Sparse Attention", "How It Works").
 //
-// How (gfx950 design, not the pages' Blackwell kernel).  This kernel takes 128-token blocks
-// with GQA pairs, and multi-head attention at d = 64; fwd_bf16_basic.hip takes the rest.
+// How (gfx950 design, not the pages' Blackwell kernel).  This kernel takes 128- and 64-token
+// blocks with GQA pairs, and multi-head attention at d = 64 with 128-token blocks;
+// fwd_bf16_basic.hip takes the rest.
 //  * Work item = (batch, GP query heads that share one key/value head, query block i).  The
-//    work-group has GP * 4 wavefronts; wavefront w owns query head w / 4 and rows
-//    [32 (w % 4), +32) of the block, so every K/V chunk staged in LDS feeds all GP heads (GQA
-//    sharing) while each wavefront keeps one head's state (<= 256 VGPRs): two wavefronts per
-//    SIMD.  The launch is persistent: as many work-groups as fit the device, each walking a
+//    work-group has GP * B / 32 wavefronts; wavefront w owns query head w / (B / 32) and 32 rows
+//    of the block, so every K/V chunk staged in LDS feeds all GP heads (GQA sharing) while each
+//    wavefront keeps one head's state (<= 256 VGPRs): two wavefronts per SIMD (one 8-wavefront
+//    work-group per CU at B = 128, two 4-wavefront ones at B = 64).  The launch is persistent: as many work-groups as fit the device, each walking a
 //    serpentine share of the items (longest rows first, the items of an XCD's share from the
 //    same heads so that its work-groups share K/V tiles in that XCD's L2).
 //  * Loop over the row's key blocks ("Block Sparse Attention in LLMs", section 6), one
-//    128-key LDS chunk per block.  Chunks are copied HBM -> LDS one chunk ahead with
+//    LDS chunk per block (128 keys, two softmax steps; or 64 keys, one step).  Chunks are copied HBM -> LDS one chunk ahead with
 //    asynchronous direct-to-LDS loads (global_load_lds_dwordx4, no register staging) into
 //    rings of two K stages and three V stages (a chunk's V outlives its K by one softmax step,
 //    see below), one barrier per chunk; the rings run on across work items, so the next item's
@@ -422,13 +423,44 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
                 exp_pack(sA, pk);
                 pv(sV[vst(c)], KC * sp, pk);
             };
-            static_assert(C::SPC == 2 && C::CPT == 1, "one key block of two softmax steps per chunk");
+            static_assert(C::CPT == 1 && (C::SPC == 2 || C::SPC == 1), "one key block per chunk, of one or two steps");
             // A valid row lists its key blocks in ascending order and ends with the diagonal
             // block i, so chunks 0 .. NCH-2 are unmasked and only the last one is causally
             // masked; the unmasked chunks run the software pipeline, whose steady state is the
             // only code inside the chunk loop.
             barrier_chunk(0);
-            if (NCH > 1) {
+            if constexpr (C::SPC == 1) {
+                // 64-token blocks: one softmax step per chunk, so step c's scores go to sB for
+                // odd c and to sA for even c; the loop takes the steps in pairs to keep the
+                // buffers compile-time
+                if (NCH > 1) {
+                    s_mma(sA, sK[kst(0)], 0);
+                    rescale(row_max(sA));
+                    int c = 1;
+                    for (; c + 1 < NCH - 1; c += 2) {
+                        barrier_chunk(c);
+                        iter(c, T_{}, S0{}, F{});
+                        barrier_chunk(c + 1);
+                        iter(c + 1, F{}, S0{}, F{});
+                    }
+                    const bool odd_tail = c < NCH - 1;  // one unmasked (odd) step left
+                    if (odd_tail) {
+                        barrier_chunk(c);
+                        iter(c, T_{}, S0{}, F{});
+                    }
+                    barrier_chunk(NCH - 1);
+                    // finish the pipeline: step NCH-2 waits in sB when odd, in sA when even
+                    if (odd_tail)
+                        exp_pack(sB, pk);
+                    else
+                        exp_pack(sA, pk);
+                    if (nxt.ok) load_q_into(qn, nxt);
+                    pv(sV[vst(NCH - 2)], 0, pk);
+                } else if (nxt.ok) {
+                    load_q_into(qn, nxt);
+                }
+                simple_step(NCH - 1, 0);
+            } else if (NCH > 1) {
                 s_mma(sA, sK[kst(0)], 0);
                 rescale(row_max(sA));
                 iter(0, T_{}, S1{}, F{});
@@ -447,8 +479,10 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
             } else if (nxt.ok) {
                 load_q_into(qn, nxt);
             }
-            simple_step(NCH - 1, 0);
-            simple_step(NCH - 1, 1);
+            if constexpr (C::SPC == 2) {
+                simple_step(NCH - 1, 0);
+                simple_step(NCH - 1, 1);
+            }
             gbase += NCH;
         } else if (nxt.ok) {
             load_q_into(qn, nxt);
@@ -527,13 +561,20 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 }  // namespace
 
 // The pipelined kernel takes 128-token blocks with GQA pairs (one 8-wavefront work-group per
-// CU) and multi-head d = 64 (two 4-wavefront work-groups per CU); the rest goes to the
-// unpipelined kernel.
+// CU), 64-token blocks with GQA pairs (two 4-wavefront work-groups per CU) and multi-head d = 64
+// at 128-token blocks (two 4-wavefront work-groups per CU); the rest goes to the unpipelined
+// kernel.
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t stream) {
     const int G = p.heads_q / p.heads_kv;
     if (block == 128 && G % 2 == 0) {
         if (d == 64) return launch<64, 128, 2, 128>(p, stream);
         if (d == 128) return launch<128, 128, 2, 128>(p, stream);
+    }
+    // 64-token blocks with GQA pairs: one 64-key step per chunk, four wavefronts per work-group
+    // and 80 KiB of LDS at d = 128, so two work-groups share a CU
+    if (block == 64 && G % 2 == 0) {
+        if (d == 64) return launch<64, 64, 2, 64>(p, stream);
+        if (d == 128) return launch<128, 64, 2, 64>(p, stream);
     }
     // One head per work-group at d = 64: the pipelined kernel pays off once rows hold more than a
     // block or two (it overlaps the next block's copy with the current one); for rows of about
