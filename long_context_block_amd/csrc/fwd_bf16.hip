@@ -423,43 +423,50 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
                 exp_pack(sA, pk);
                 pv(sV[vst(c)], KC * sp, pk);
             };
-            static_assert(C::CPT == 1 && (C::SPC == 2 || C::SPC == 1), "one key block per chunk, of one or two steps");
+            static_assert((C::CPT == 1 && C::SPC == 2) || (C::SPC == 1 && (C::CPT == 1 || C::CPT == 2)),
+                          "a block is one chunk of two steps, or one or two chunks of one step");
             // A valid row lists its key blocks in ascending order and ends with the diagonal
-            // block i, so chunks 0 .. NCH-2 are unmasked and only the last one is causally
-            // masked; the unmasked chunks run the software pipeline, whose steady state is the
-            // only code inside the chunk loop.
+            // block i, so only the chunks of the last block are causally masked; the unmasked
+            // chunks run the software pipeline, whose steady state is the only code inside the
+            // chunk loop.
             barrier_chunk(0);
             if constexpr (C::SPC == 1) {
-                // 64-token blocks: one softmax step per chunk, so step c's scores go to sB for
-                // odd c and to sA for even c; the loop takes the steps in pairs to keep the
-                // buffers compile-time
-                if (NCH > 1) {
+                // One softmax step per 64-key chunk, so step c's scores go to sB for odd c and to
+                // sA for even c; the loop takes the steps in pairs to keep the buffers
+                // compile-time.  Chunks 0 .. NU-1 are unmasked, the last CPT (the diagonal
+                // block) masked.
+                const int NU = NCH - C::CPT;
+                if (NU > 0) {
                     s_mma(sA, sK[kst(0)], 0);
                     rescale(row_max(sA));
                     int c = 1;
-                    for (; c + 1 < NCH - 1; c += 2) {
+                    for (; c + 1 < NU; c += 2) {
                         barrier_chunk(c);
                         iter(c, T_{}, S0{}, F{});
                         barrier_chunk(c + 1);
                         iter(c + 1, F{}, S0{}, F{});
                     }
-                    const bool odd_tail = c < NCH - 1;  // one unmasked (odd) step left
+                    const bool odd_tail = c < NU;  // one unmasked (odd) step left
                     if (odd_tail) {
                         barrier_chunk(c);
                         iter(c, T_{}, S0{}, F{});
                     }
-                    barrier_chunk(NCH - 1);
-                    // finish the pipeline: step NCH-2 waits in sB when odd, in sA when even
+                    barrier_chunk(NU);
+                    // finish the pipeline: step NU-1 waits in sB when odd, in sA when even
                     if (odd_tail)
                         exp_pack(sB, pk);
                     else
                         exp_pack(sA, pk);
                     if (nxt.ok) load_q_into(qn, nxt);
-                    pv(sV[vst(NCH - 2)], 0, pk);
+                    pv(sV[vst(NU - 1)], 0, pk);
                 } else if (nxt.ok) {
                     load_q_into(qn, nxt);
                 }
-                simple_step(NCH - 1, 0);
+                simple_step(NU, 0);
+                if constexpr (C::CPT == 2) {
+                    barrier_chunk(NU + 1);
+                    simple_step(NU + 1, 0);
+                }
             } else if (NCH > 1) {
                 s_mma(sA, sK[kst(0)], 0);
                 rescale(row_max(sA));
@@ -581,6 +588,9 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, int block, hipStream_t str
     // one block (the block-diagonal route) the one-item-per-work-group kernel is a little faster
     // (18.0 vs 18.7 us at 2 x 8 heads, n 8192).
     if (block == 128 && d == 64 && 2 * p.nnz > 3 * (int64_t)p.nqb) return launch<64, 128, 1, 128>(p, stream);
+    // Multi-head d = 128 at 128-token blocks: 64-key chunks (two per block), so that two
+    // 4-wavefront work-groups (80 KiB of LDS each) share a CU
+    if (block == 128 && d == 128 && 2 * p.nnz > 3 * (int64_t)p.nqb) return launch<128, 128, 1, 64>(p, stream);
     return launch_fwd_bf16_basic(p, d, block, stream);
 }
 
