@@ -142,8 +142,19 @@ void bwd_dq_kernel(BwdParams p) {
             }
         // dS^T = P^T (dP^T - D), packed to bf16; masked pairs (future keys on the diagonal block,
         // malformed entries, rows past n) have P = 0
-        const bool diag = (j == i);
-        const int lim = (j < 0 || !row_ok) ? -1 : (diag ? qloc - kb : kCh);
+        // Only the diagonal block (and a malformed entry) has excluded pairs: their scores become
+        // -inf in place, so that P = exp2(-inf) = 0 below; a row past n has dO = 0, hence dP = D =
+        // 0 and dS = 0, with no mask.
+        if (j == i || j < 0) {
+            const int lim = (j < 0) ? -1 : qloc - kb;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * c2 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    s[c2][r] = key > lim ? -__builtin_inff() : s[c2][r];
+                }
+        }
         uint32_t pk[2][8];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
@@ -153,8 +164,7 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 2 * x + e;
-                    const int key = 32 * c2 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    const float pw = key > lim ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[c2][r], p.scale_log2, -lse2));
+                    const float pw = __builtin_amdgcn_exp2f(fmaf(s[c2][r], p.scale_log2, -lse2));
                     ds[e] = pw * (dp[c2][r] - dval);
                 }
                 pk[c2][x] = pack_bf16x2(ds[0], ds[1]);
