@@ -473,9 +473,15 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
                 iter(0, T_{}, S1{}, F{});
                 for (int c = 1; c < NCH - 1; ++c) {
                     barrier_chunk(c);
+                    // The SIMD arbiter favours the older wavefront (the first head's), which
+                    // reaches each barrier first; for the second step of a chunk the second
+                    // head's wavefronts take the higher priority, so both arrive together.
+                    __builtin_amdgcn_s_setprio(0);
                     iter(c, F{}, S0{}, F{});
+                    if (g == 1) __builtin_amdgcn_s_setprio(1);
                     iter(c, T_{}, S1{}, F{});
                 }
+                __builtin_amdgcn_s_setprio(0);
                 barrier_chunk(NCH - 1);
                 // finish the pipeline (step (NCH-2, 1) waits in sB)
                 exp_pack(sB, pk);
