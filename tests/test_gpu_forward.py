@@ -410,3 +410,56 @@ def test_nan_reaches_only_the_rows_that_read_it(case, which):
         for r_ok in zip(*np.nonzero(may & ~must)):  # the rows before j in its diagonal block
             x0, x1 = a0[r_ok], a1[r_ok]
             assert np.isnan(x1).all() or same(x0, x1)
+
+
+# ---- malformed routes: results undefined, every access in bounds -----------------------------
+
+def malformed_route(nqb, nnz, seed):
+    """A route that breaks every rule bsa_check_route enforces: row pointers that decrease, jump
+    past nnz and repeat (empty rows), and entries that are negative, in the future or repeated."""
+    rng = np.random.default_rng(seed)
+    rp = np.sort(rng.integers(0, nnz + 1, size=nqb + 1))
+    rp[0] = 0
+    rp[1::3] = rp[1::3][::-1]           # non-monotone
+    rp[-1] = nnz + 7                    # past the end
+    rp[nqb // 2] = rp[nqb // 2 - 1]     # an empty row
+    ci = rng.integers(-3, nqb + 3, size=nnz)
+    return (torch.tensor(rp.astype(np.int32), device="cuda"), torch.tensor(ci.astype(np.int32), device="cuda"))
+
+
+MALFORMED_CASES = [
+    # (name, heads_q, heads_kv, n, d, block, dtype): each forward kernel family
+    ("gqa2-d128-b128", 4, 2, 700, 128, 128, "bf16"),   # pipelined, 128-key chunks
+    ("gqa2-d128-b64", 4, 2, 700, 128, 64, "bf16"),     # pipelined, one 64-key chunk per block
+    ("mha-d128-b128", 2, 2, 700, 128, 128, "bf16"),    # pipelined, two 64-key chunks per block
+    ("mha-d64-b128", 2, 2, 700, 64, 128, "bf16"),      # pipelined, multi-head d = 64
+    ("mha-d128-b64", 2, 2, 700, 128, 64, "bf16"),      # unpipelined
+    ("mha-d64-b128-fp32", 2, 2, 700, 64, 128, "fp32"), # fp32
+]
+
+
+@pytest.mark.parametrize("case", MALFORMED_CASES, ids=[c[0] for c in MALFORMED_CASES])
+def test_malformed_route_stays_in_bounds(case):
+    """Without BSA_VALIDATE_ROUTE a malformed route gives undefined output, but no store leaves the
+    caller's O and LSE buffers, and the same buffers then serve a valid route correctly."""
+    from canary import padded
+    name, hq, hkv, n, d, B, dtype = case
+    w = synth.WORKLOADS["qwen3_32k"].resized(name=name, heads_q=hq, heads_kv=hkv, n=n, d=d, block=B, dtype=dtype)
+    q, k, v = (x.cuda() for x in synth.make_qkv(w))
+    nqb = w.nqb
+    for seed in (1, 2):
+        rp, ci = malformed_route(nqb, 3 * nqb, seed)  # nnz > 1.5 nqb: the multi-head rows count as long
+        print(f"malformed {name} seed={seed}: row_ptr={rp.tolist()}", flush=True)
+        o = padded(q.shape, q.dtype)
+        lse = padded(q.shape[:3], torch.float32)
+        bsa.bsa_forward(q, k, v, o.t, rp, ci, B, lse=lse.t)
+        torch.cuda.synchronize()
+        assert o.guards_intact() and lse.guards_intact()
+    # a valid route afterwards, through the same entry point
+    (rp, ci), (orp, oci) = workload_routes(w)
+    o = bsa.forward(q, k, v, rp, ci, B)
+    torch.cuda.synchronize()
+    ref = A.attention(*(x.cpu() for x in (q, k, v)), B, orp, oci)
+    mx, rl2 = errors(o.float().cpu().numpy(), ref)
+    ma, rt = tol(w.torch_dtype)
+    assert mx <= ma and rl2 <= rt
