@@ -31,10 +31,13 @@ HIPCC_FLAGS = [
 ]
 # Per-source extras.  fwd_bf16.hip keeps MFMA results in VGPRs: two wavefronts per SIMD, and the
 # rare rescale multiplies the accumulators in place instead of shuttling them through AGPRs.
+# bwd_dkdv.hip likewise: its scores feed the vector unit directly, and its resident K, V operands
+# go to AGPRs instead.
 EXTRA_FLAGS = {
     "fwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
     "fwd_bf16_basic.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
     "bwd_bf16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    "bwd_dkdv.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 

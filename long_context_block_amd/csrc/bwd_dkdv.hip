@@ -20,8 +20,10 @@
 //    transposed by the LDS unit (ds_read_b64_tr_b16).  Software pipeline: S, dP of sub-chunk
 //    t + 1 are issued to the matrix cores one instruction at a time between the exponentials and
 //    dS of sub-chunk t.  The accumulation order per accumulator is the plain sequential one.
-//    The file is compiled with the MFMA accumulators allowed in AGPRs: dK, dV (and S, dP) live
-//    there, which leaves the 256 architectural VGPRs to K, V, P, dS and the operand rings.
+//    The file is compiled with the MFMA results in VGPRs (--amdgpu-mfma-vgpr-form): dK, dV, S and
+//    dP take the 256 architectural VGPRs, and the compiler moves the resident K, V operands (which
+//    the matrix cores read from either file) to AGPRs, so the vector unit reads S, dP without
+//    copying them out of the accumulation registers first (one wavefront per SIMD either way).
 //  * A key block read by many query blocks (block 0 in BF1 is read by all of them) is split into
 //    segments of at most kSeg units so that no work-group carries a whole column; a block of one
 //    segment stores bf16 dK, dV directly, otherwise each segment writes fp32 partials that
