@@ -126,6 +126,22 @@ def test_splitmix64_known_answer(golden):
     assert got == [int(v, 16) for v in vals]
 
 
+def test_pair_hash_composition_known_answer(golden):
+    """h(seed, i, j) = SM(seed XOR SM((i << 32) | j)) pinned by the same published vector: with i, j
+    the high and low halves of the golden-ratio increment the inner call is SM(gamma), the second
+    printed output; a seed equal to that output XOR 2 gamma turns the outer call into SM(2 gamma), the
+    third.  A swapped (j, i) packing, a missing inner or outer step, or a sum in place of the XOR
+    would each miss the printed value."""
+    _, vals = golden("splitmix64_seed0.txt")
+    ka = [int(v, 16) for v in vals]
+    gamma, m64 = 0x9E3779B97F4A7C15, (1 << 64) - 1
+    hi, lo = gamma >> 32, gamma & 0xFFFFFFFF
+    assert R.pair_hash(ka[1] ^ ((2 * gamma) & m64), hi, lo) == ka[2]
+    # i = j = 0: the inner call is SM(0), the first printed output
+    assert R.pair_hash(ka[0] ^ gamma, 0, 0) == ka[1]
+    assert R.pair_hash(ka[1] ^ ((2 * gamma) & m64), lo, hi) != ka[2]
+
+
 @pytest.mark.parametrize("n_random,keep_first", [(14, True), (3, False)])
 def test_static_random_structure(n_random, keep_first):
     nqb = 160
