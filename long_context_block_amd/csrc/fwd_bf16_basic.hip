@@ -1,6 +1,7 @@
 // fwd_bf16_basic.hip — unpipelined bfloat16 block-sparse attention forward on gfx950 matrix
-// cores, for the shapes the pipelined kernel (fwd_bf16.hip) does not take: 64-token blocks and
-// multi-head attention at d = 128.
+// cores, for the shapes the pipelined kernel (fwd_bf16.hip) does not take: rows that average at
+// most about a block and a half without a GQA pair (the block-diagonal route), where one work
+// item per work-group beats the persistent walk.
 //
 // What it computes: for every (batch, query head, query block i), exact softmax attention of
 // the block's queries over the keys of the key blocks listed in row i of the CSR route, with
