@@ -187,7 +187,8 @@ struct BwdParams {
     float* lse2;      // workspace: lse * log2(e) [batch, heads_q, n_pad], +inf past n
     float* ld_pad;    // workspace: 32 x +inf, then 32 x 0: lse2 and D of a fully excluded row run
     int32_t* seg_ptr; // workspace: [nqb + 1] segment prefix of the transposed rows
-    int32_t* seg_info;// workspace: [nseg_ub, 4] per segment: key block, index within it, segments of the block
+    int32_t* seg_info;// workspace: [nseg_ub, 4] per segment: key block, its first transposed entry, the segment's
+                      // first unit, its sub-chunk count (| 1 << 16 when the block has one segment)
     float* part;      // workspace: [batch * heads_kv * nseg_ub, 2, block, d] partial dK, dV
     int32_t batch, heads_q, heads_kv;
     int32_t nqb;

@@ -207,14 +207,19 @@ __global__ __launch_bounds__(1024) void bwd_seg_kernel(BwdParams p, int cpb) {
     const int G = p.heads_q / p.heads_kv;
     const int64_t per = (nqb + 1023) / 1024;
     const int64_t r0 = t * per, r1 = (r0 + per < nqb) ? r0 + per : nqb;
-    auto segs = [&](int64_t j) -> int64_t {
-        int64_t a = p.t_row_ptr[j], z = p.t_row_ptr[j + 1];
+    // key block j's first transposed entry a (clamped), its unit count c and its segment count
+    auto seg_of = [&](int64_t j, int64_t& a, int64_t& c) -> int64_t {
+        a = p.t_row_ptr[j];
+        int64_t z = p.t_row_ptr[j + 1];
         a = a < 0 ? 0 : (a > p.nnz ? p.nnz : a);
         z = z < a ? a : (z > p.nnz ? p.nnz : z);
-        const int64_t len = z - a;
-        const int64_t c = len * G * cpb;
+        c = (z - a) * G * cpb;
         const int64_t s = (c + kSeg - 1) / kSeg;
         return s > 1 ? s : 1;
+    };
+    auto segs = [&](int64_t j) -> int64_t {
+        int64_t a, c;
+        return seg_of(j, a, c);
     };
     int64_t local = 0;
     for (int64_t j = r0; j < r1; ++j) local += segs(j);
@@ -227,11 +232,20 @@ __global__ __launch_bounds__(1024) void bwd_seg_kernel(BwdParams p, int cpb) {
         __syncthreads();
     }
     int64_t run = part[t] - local;
+    // per segment: key block, first transposed entry of the block, first unit, and the segment's
+    // 32-query sub-chunk count (at most 2 kSeg) with bit 16 set when the block has one segment;
+    // the block's units are dealt evenly over its segments (at most kSeg each)
     for (int64_t j = r0; j < r1; ++j) {
         p.seg_ptr[j] = (int32_t)run;
-        const int64_t sj = segs(j);
-        for (int64_t s = 0; s < sj && run + s < p.nseg_ub; ++s)
-            *(int4*)(p.seg_info + 4 * (run + s)) = make_int4((int)j, (int)s, (int)sj, 0);
+        int64_t a, c;
+        const int64_t sj = seg_of(j, a, c);
+        int64_t per = (c + sj - 1) / sj;
+        per = per < kSeg ? per : kSeg;
+        for (int64_t s = 0; s < sj && run + s < p.nseg_ub; ++s) {
+            const int64_t ub = s * per, ue = (ub + per < c) ? ub + per : c;
+            const int nsub = ue > ub ? (int)(2 * (ue - ub)) : 0;
+            *(int4*)(p.seg_info + 4 * (run + s)) = make_int4((int)j, (int)a, (int)ub, nsub | (sj == 1 ? 1 << 16 : 0));
+        }
         run += sj;
     }
     if (t == 1023) p.seg_ptr[nqb] = (int32_t)part[1023];

@@ -60,30 +60,57 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int64_t bg = blockIdx.x / p.nseg_ub;  // batch * heads_kv + g
     const int sw = (int)(blockIdx.x % p.nseg_ub);
     const int64_t nqb = p.nqb;
-    if (sw >= p.seg_ptr[nqb]) return;
-    // key block j of this segment, its index within the block and the block's segment count
+    // the segment's descriptor (written by the segment kernel) is read together with the segment
+    // count, so the work-group's first dependent load is the sub-chunk table below
     const int4 info = *(const int4*)(p.seg_info + 4 * (int64_t)sw);
-    const int j = info.x, seg = info.y, nseg = info.z;
+    const int nsegs = p.seg_ptr[nqb];
+    // (both reads feed the exit test, so they are issued together; a valid descriptor has
+    // info.w >= 0, and slots past the segment count hold stale values that are not used)
+    if ((sw >= nsegs) | (info.w < 0)) return;
+    const int j = info.x;                       // key block
+    const int64_t t0 = info.y;                  // its first transposed entry
+    const int u_begin = info.z;                 // the segment's first unit
+    const int NSUB = info.w & 0xffff;           // its 32-query sub-chunks
+    const bool single = (info.w >> 16) & 1;     // the block has one segment
     const int64_t b = bg / p.heads_kv, g = bg % p.heads_kv;
     const int G = p.heads_q / p.heads_kv;
     const int64_t n = p.n, n_pad = p.n_pad;
-
-    int64_t t0 = p.t_row_ptr[j], t1 = p.t_row_ptr[j + 1];
-    t0 = t0 < 0 ? 0 : (t0 > p.nnz ? p.nnz : t0);
-    t1 = t1 < t0 ? t0 : (t1 > p.nnz ? p.nnz : t1);
     const int upt = G * UPB;  // units per entry of the transposed row
-    const int units_all = (int)(t1 - t0) * upt;
-    // the block's units dealt evenly over its nseg = ceil(units / kSeg) segments (<= kSeg each)
-    int per_seg = nseg > 0 ? (units_all + nseg - 1) / nseg : 0;
-    per_seg = per_seg < kSeg ? per_seg : kSeg;
-    const int u_begin = seg * per_seg;
-    const int u_end = (u_begin + per_seg < units_all) ? u_begin + per_seg : units_all;
-    const int NSUB = u_end > u_begin ? 2 * (u_end - u_begin) : 0;
 
     // Sub-chunk table: lane x describes sub-chunks x (index 0) and 64 + x (index 1) by batch *
     // query head, first query row, and kind: the row's offset within the diagonal block
     // (0 .. BLK - 1), BLK off the diagonal, -1 for an entry that is no causal reader of j.
+    // Both route reads are issued before the K, V rows below and before any wait (indices
+    // clamped to the route, results of lanes past the segment unused).
     static_assert(2 * kSeg <= 128, "two sub-chunks per lane");
+    int iqv[2] = {0, 0};
+    const int64_t last = p.nnz - 1;
+    if (last >= 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int x = 64 * h + lane;
+            const int u = u_begin + (x >> 1);
+            const int64_t e = t0 + u / upt;
+            iqv[h] = p.t_col_idx[e < last ? e : last];
+        }
+    }
+
+    // this wavefront's 32 keys, resident as B operands: K[key][16kk + 8hf ..], V likewise (rows
+    // past n read row 0 and are zeroed)
+    const int kloc = 32 * wv + l32;
+    const int64_t krow = (int64_t)j * BLK + kloc;
+    const bool key_ok = krow < n;
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const __bf16* Kr = (const __bf16*)p.k + (bg * n + (key_ok ? krow : 0)) * D;
+        const __bf16* Vr = (const __bf16*)p.v + (bg * n + (key_ok ? krow : 0)) * D;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            kf[kk] = *(const bf16x8*)(Kr + 16 * kk + 8 * hf);
+            vf[kk] = *(const bf16x8*)(Vr + 16 * kk + 8 * hf);
+        }
+    }
+
     int tbh[2], tq0[2], tkind[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -93,8 +120,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         tkind[h] = -1;
         if (x < NSUB) {
             const int u = u_begin + (x >> 1);
-            const int ti = u / upt, rem = u - ti * upt;
-            const int iq = p.t_col_idx[t0 + ti];
+            const int rem = u % upt;
+            const int iq = iqv[h];
             const bool bad = iq < j || iq >= nqb;
             const int i = bad ? j : iq;
             tbh[h] = (int)(b * p.heads_q + g * G) + rem / UPB;
@@ -119,18 +146,11 @@ void bwd_dkdv_kernel(BwdParams p) {
         NM = pre ? c0 + c1 : NSUB;
     }
 
-    // this wavefront's 32 keys, resident as B operands: K[key][16kk + 8hf ..], V likewise
-    const int kloc = 32 * wv + l32;
-    const int64_t krow = (int64_t)j * BLK + kloc;
-    const bool key_ok = krow < n;
-    bf16x8 kf[D / 16], vf[D / 16];
-    {
-        const __bf16* Kr = (const __bf16*)p.k + (bg * n + (key_ok ? krow : 0)) * D;
-        const __bf16* Vr = (const __bf16*)p.v + (bg * n + (key_ok ? krow : 0)) * D;
+    if (!key_ok) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            kf[kk] = key_ok ? *(const bf16x8*)(Kr + 16 * kk + 8 * hf) : bf16x8{};
-            vf[kk] = key_ok ? *(const bf16x8*)(Vr + 16 * kk + 8 * hf) : bf16x8{};
+            kf[kk] = bf16x8{};
+            vf[kk] = bf16x8{};
         }
     }
     f32x16 dk[D / 32], dv[D / 32];
@@ -378,7 +398,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
 
     // lane holds d = 32 db + 8 j4 + 4 hf + (0..3) of key kloc
-    if (nseg == 1) {
+    if (single) {
         if (key_ok) {
             __bf16* Dk = (__bf16*)p.dk + (bg * n + krow) * D;
             __bf16* Dv = (__bf16*)p.dv + (bg * n + krow) * D;
