@@ -101,6 +101,10 @@ REDUCED = [
     synth.WORKLOADS["bf1_4k"].resized(name="gqa4-d64-b64", n=600, d=64, heads_q=4, heads_kv=1),
     synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-ragged", n=1, heads_q=2, heads_kv=1),
     synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-ragged-129", n=129, heads_q=2, heads_kv=1),
+    # batch > 1 with GQA pairs and a ragged last block (the transposed rows and the segment table
+    # are per key/value head of each batch entry)
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-d128-b128-batch2-ragged", n=1100, batch=2, heads_q=4, heads_kv=2),
+    synth.WORKLOADS["bf1_4k"].resized(name="gqa2-d128-b64-batch3-ragged", n=650, batch=3, heads_q=4, heads_kv=2),
 ]
 
 

@@ -138,6 +138,27 @@ def test_parity_full_size_b64_sampled(kind):
     check(w, kind=kind, rows=rows)
 
 
+# Persistent launches whose items do not split evenly over the XCDs (the plain serpentine walk),
+# several items per work-group, batch > 1 and a ragged last block, for the three pipelined
+# instantiations that take the pages' shapes: 128-token blocks with GQA pairs, multi-head d = 128
+# with 64-key chunks, 64-token blocks with GQA pairs.
+MANY_ITEMS = [
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa-pairs-b128-batch3-ragged", batch=3, heads_q=6, heads_kv=3, n=33000),
+    synth.WORKLOADS["static_random_64k"].resized(name="mha-b128-batch2-ragged", batch=2, heads_q=5, heads_kv=5,
+                                                 n=20000),
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa-pairs-b64-batch2-ragged", batch=2, heads_q=6, heads_kv=3,
+                                         n=17000, block=64),
+]
+
+
+@pytest.mark.parametrize("w", MANY_ITEMS, ids=[w.name for w in MANY_ITEMS])
+def test_parity_many_items_per_workgroup_sampled(w):
+    total = w.batch * (w.heads_q // 2 if (w.heads_q // w.heads_kv) % 2 == 0 else w.heads_q) * -(-w.n // w.block)
+    assert total % 8 != 0 and total > 512  # the walk without XCD ranges, several items per work-group
+    rows = sample_rows(w.n, w.block, np.random.default_rng(21), extra=12)
+    check(w, rows=rows)
+
+
 def test_parity_full_size_dense_route_sampled():
     w = synth.WORKLOADS["qwen3_32k"]
     rows = sample_rows(w.n, w.block, np.random.default_rng(8), extra=8)
