@@ -87,8 +87,11 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront index (uniform)
     const int l32 = lane & 31;
     const int hf = lane >> 5;
-    const int g = wv / C::NWQ;                  // this wavefront's head within the group
-    const int qloc = 32 * (wv % C::NWQ) + l32;  // query row within the block
+    const int g = wv / C::NWQ;  // this wavefront's head within the group
+    // 32-row group of the block: the second head takes the groups in reverse order, so that the two
+    // wavefronts of a SIMD (wavefronts w and w + NWQ) hold an early and a late group of rows
+    const int rg = (GP == 2 && g == 1) ? C::NWQ - 1 - wv % C::NWQ : wv % C::NWQ;
+    const int qloc = 32 * rg + l32;  // query row within the block
     const int64_t n = p.n;
     const int hgroups = p.heads_q / GP;
     const int hpk = p.heads_q / p.heads_kv;
@@ -494,7 +497,9 @@ void fwd_bf16_kernel(FwdParams p, int64_t total) {
             }
             if constexpr (C::SPC == 2) {
                 simple_step(NCH - 1, 0);
-                simple_step(NCH - 1, 1);
+                // the diagonal block's second step holds keys later than every row of the first
+                // KC / 32 row groups: fully masked there, so those wavefronts skip it
+                if (32 * rg + 31 >= KC) simple_step(NCH - 1, 1);
             }
             gbase += NCH;
         } else if (nxt.ok) {
