@@ -125,7 +125,7 @@ void bwd_dq_kernel(BwdParams p) {
         const int64_t j = block_of(ch);
         const int kb = kCh * (ch % CPB);  // first key of the chunk within its block
         // a chunk of the diagonal block whose keys all follow this wavefront's 32 rows adds
-        // exactly nothing (P = 0): skipped
+        // exactly nothing (P = 0): skipped (the test has one value per wavefront)
         if (j == i && kb > 32 * wv + 31) continue;
         // S^T and dP^T for the chunk's 64 keys (two 32-key accumulators each)
         f32x16 s[2], dp[2];
