@@ -102,6 +102,10 @@ REDUCED = [
                                          n_random=5),
     synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-d64-b64-sliding", n=999, d=64, block=64, heads_q=4, heads_kv=2,
                                          route_kind=R.SLIDING_WINDOW, n_local=3, batch=2),
+    # multi-head d = 64 at 128-token blocks over rows of several blocks (the pipelined kernel with
+    # 128-key chunks and one head per work-group), and odd GQA groups at d = 128
+    synth.WORKLOADS["qwen3_32k"].resized(name="mha-d64-b128-bf1", n=1500, d=64, heads_q=3, heads_kv=3),
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa3-d128-b128-bf1", n=1400, heads_q=6, heads_kv=2),
 ]
 
 
