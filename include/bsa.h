@@ -141,6 +141,10 @@ bsa_status bsa_build_route_transpose(const int32_t* row_ptr, const int32_t* col_
  * Supported: d in {64, 128}; block in {64, 128}; dtype BF16 or FP32; any n >= 0 (the last block
  * may be partial; batch == 0 or n == 0 is a no-op).  BF16 output is rounded to nearest-even
  * from fp32; the bf16 path rounds the softmax weights to bf16 before the PV product.
+ * Non-finite inputs: a NaN in a q row makes that output row (and its lse) NaN; a NaN in a key
+ * or value row reaches the output rows that select that key; rows of the same diagonal block
+ * that precede the key may show it too (they share its matrix product); every other output
+ * row is bit-identical to the run without it.
  */
 bsa_status bsa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                        int32_t batch, int32_t heads_q, int32_t heads_kv, int64_t n, int32_t d,
