@@ -106,6 +106,8 @@ REDUCED = [
     # 128-key chunks and one head per work-group), and odd GQA groups at d = 128
     synth.WORKLOADS["qwen3_32k"].resized(name="mha-d64-b128-bf1", n=1500, d=64, heads_q=3, heads_kv=3),
     synth.WORKLOADS["qwen3_32k"].resized(name="gqa3-d128-b128-bf1", n=1400, heads_q=6, heads_kv=2),
+    # GQA pairs at d = 64 and 128-token blocks (the headline kernel's d = 64 instantiation)
+    synth.WORKLOADS["qwen3_32k"].resized(name="gqa2-d64-b128-bf1", n=1300, d=64, heads_q=4, heads_kv=2, batch=2),
 ]
 
 
